@@ -1,0 +1,23 @@
+"""CPU oracle for the stage-task path -- TEST INFRASTRUCTURE, not product code.
+
+A plain, slow, float64 NumPy statement of what one stage task computes (one DiT
+Transformer block at one denoising step for one latent chunk, reading the noisy
+KV that earlier chunks left at that same step) and of the two chunk x step
+schedules (sequential, staggered).  It shares no code with the HIP path; only
+the seeded generators in ``synthetic`` serve both.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  The product path never routes through it.
+
+Parity status: every function is pinned by a ``-m "not gpu"`` test against a
+closed form, a library routine, brute force or an invariant (see
+``tests/test_oracle_*.py``).  The absolute values of a whole block are fixed
+only by the readings of the pages listed in the design notes; the pages print
+no worked numeric example of the block.
+"""
+from .block import (  # noqa: F401
+    attention, block_task, context_kv, gelu_tanh, layer_norm, modulation,
+    qkv_phase, rest_phase, rope3d, rope_segments, silu, sinusoid, time_embedding,
+    token_positions,
+)
+from .schedule import RingPool, run_schedule, staggered_ticks  # noqa: F401

@@ -1,0 +1,287 @@
+"""Pins of the CPU oracle's block math against closed forms, library routines,
+brute force and invariants (no GPU).
+
+Each pin is chosen so that a plausible slip in the oracle -- a dropped term, a
+wrong sign or index, a swapped operand, a wrong modulation row -- fails it."""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from synthetic import C1, inputs, with_
+
+torch.set_default_dtype(torch.float64)
+
+
+def T(a):
+    return torch.as_tensor(np.asarray(a, dtype=np.float64))
+
+
+# ---------------------------------------------------------------- attention
+def brute_attention(q, k, v):
+    """Triple loop, float64, softmax written out per query."""
+    Lq, H, d = q.shape
+    out = np.zeros_like(q)
+    for h in range(H):
+        for i in range(Lq):
+            logits = [sum(q[i, h, t] * k[j, h, t] for t in range(d)) / math.sqrt(d)
+                      for j in range(k.shape[0])]
+            m = max(logits)
+            ws = [math.exp(x - m) for x in logits]
+            z = sum(ws)
+            for t in range(d):
+                out[i, h, t] = sum(ws[j] * v[j, h, t] for j in range(k.shape[0])) / z
+    return out
+
+
+def test_attention_brute_force():
+    r = np.random.default_rng(1)
+    q = r.standard_normal((5, 2, 4)) * 2.0   # peaked softmax
+    k = r.standard_normal((7, 2, 4)) * 2.0
+    v = r.standard_normal((7, 2, 4))
+    np.testing.assert_allclose(oracle.attention(q, k, v), brute_attention(q, k, v),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_attention_matches_sdpa():
+    r = np.random.default_rng(2)
+    q = r.standard_normal((33, 3, 16))
+    k = r.standard_normal((70, 3, 16))
+    v = r.standard_normal((70, 3, 16))
+    ref = F.scaled_dot_product_attention(T(q).transpose(0, 1), T(k).transpose(0, 1),
+                                         T(v).transpose(0, 1)).transpose(0, 1).numpy()
+    np.testing.assert_allclose(oracle.attention(q, k, v), ref, rtol=1e-11, atol=1e-12)
+
+
+def test_attention_single_key_is_value():
+    r = np.random.default_rng(3)
+    q = r.standard_normal((4, 2, 8))
+    k = r.standard_normal((1, 2, 8))
+    v = r.standard_normal((1, 2, 8))
+    np.testing.assert_array_equal(oracle.attention(q, k, v), np.broadcast_to(v, q.shape))
+
+
+def test_attention_large_logits_stable():
+    q = np.full((2, 1, 4), 300.0)
+    k = np.stack([np.full((1, 4), 300.0), np.full((1, 4), -300.0)])
+    v = np.array([[[1.0, 2, 3, 4]], [[5.0, 6, 7, 8]]])
+    out = oracle.attention(q, k, v)
+    assert np.all(np.isfinite(out))
+    np.testing.assert_allclose(out[0, 0], [1, 2, 3, 4])
+
+
+# ---------------------------------------------------------------- elementwise
+def test_layer_norm_matches_library_and_moments():
+    r = np.random.default_rng(4)
+    z = r.standard_normal((9, 37)) * 3 + 5
+    ref = F.layer_norm(T(z), (37,), eps=1e-6).numpy()
+    got = oracle.layer_norm(z)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got.mean(axis=1), 0, atol=1e-12)
+    np.testing.assert_allclose(got.var(axis=1), 37 / 37 * (z.var(axis=1) / (z.var(axis=1) + 1e-6)),
+                               rtol=1e-12)
+
+
+def test_layer_norm_constant_row_is_zero():
+    np.testing.assert_array_equal(oracle.layer_norm(np.full((2, 8), 3.25)), 0.0)
+
+
+def test_gelu_tanh_matches_library():
+    z = np.linspace(-8, 8, 2001)
+    ref = F.gelu(T(z), approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(z), ref, rtol=1e-12, atol=1e-15)
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+
+
+def test_silu_matches_library():
+    z = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(oracle.silu(z), F.silu(T(z)).numpy(), rtol=1e-12, atol=1e-300)
+
+
+# ---------------------------------------------------------------- timestep features
+def test_sinusoid_special_values():
+    p0 = oracle.sinusoid(0.0)
+    np.testing.assert_array_equal(p0[:128], 1.0)
+    np.testing.assert_array_equal(p0[128:], 0.0)
+    # feature 0 has angular frequency 1000 per unit t: t = pi/2000 -> angle pi/2
+    p = oracle.sinusoid(math.pi / 2000)
+    assert abs(p[0]) < 1e-15 and abs(p[128] - 1) < 1e-15
+    # feature 64 has frequency 1000 * 10000^-0.5 = 10: t = pi/20 -> angle pi/2
+    p = oracle.sinusoid(math.pi / 20)
+    assert abs(p[64]) < 1e-14 and abs(p[128 + 64] - 1) < 1e-14
+    # cos^2 + sin^2 = 1 for every frequency
+    p = oracle.sinusoid(0.37)
+    np.testing.assert_allclose(p[:128] ** 2 + p[128:] ** 2, 1.0, rtol=1e-14)
+
+
+def test_time_embedding_library_composition():
+    D = 24
+    r = np.random.default_rng(5)
+    tw = {"wt1": r.standard_normal((256, D)) * 0.1, "bt1": r.standard_normal(D),
+          "wt2": r.standard_normal((D, D)) * 0.3, "bt2": r.standard_normal(D),
+          "wp": r.standard_normal((D, 6 * D)) * 0.3, "bp": r.standard_normal(6 * D)}
+    t = 0.625
+    half = torch.arange(128, dtype=torch.float64)
+    ang = 1000 * t * torch.pow(torch.tensor(10000.0), -half / 128)
+    phi = torch.cat([torch.cos(ang), torch.sin(ang)])
+    u = F.linear(F.silu(F.linear(phi, T(tw["wt1"]).T, T(tw["bt1"]))), T(tw["wt2"]).T, T(tw["bt2"]))
+    e = F.linear(F.silu(u), T(tw["wp"]).T, T(tw["bp"])).view(6, D).numpy()
+    np.testing.assert_allclose(oracle.time_embedding(t, tw), e, rtol=1e-12, atol=1e-12)
+
+
+def test_time_embedding_row_order():
+    """bp row r must land in modulation row r (no transposed reshape)."""
+    D = 8
+    tw = {"wt1": np.zeros((256, D)), "bt1": np.zeros(D), "wt2": np.zeros((D, D)),
+          "bt2": np.zeros(D), "wp": np.zeros((D, 6 * D)), "bp": np.arange(6 * D, dtype=float)}
+    e = oracle.time_embedding(0.3, tw)
+    np.testing.assert_array_equal(e, np.arange(6 * D, dtype=float).reshape(6, D))
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_segments():
+    assert oracle.rope_segments(128) == (44, 42, 42)
+    assert oracle.rope_segments(64) == (24, 20, 20)
+
+
+def test_token_positions_row_major():
+    pos = oracle.token_positions(3, (2, 3, 4))
+    assert pos.shape == (24, 3)
+    n = (1 * 3 + 2) * 4 + 1
+    assert tuple(pos[n]) == (3 * 2 + 1, 2, 1)
+    assert tuple(pos[0]) == (6, 0, 0)
+
+
+def _rope_complex(x, pos):
+    """3D RoPE as complex multiplication with torch.polar, per segment."""
+    L, H, d = x.shape
+    angs = []
+    for a, da in enumerate(oracle.rope_segments(d)):
+        theta = torch.pow(torch.tensor(10000.0), -torch.arange(0, da, 2, dtype=torch.float64) / da)
+        angs.append(T(pos[:, a])[:, None] * theta[None, :])
+    ang = torch.cat(angs, dim=1)
+    rot = torch.polar(torch.ones_like(ang), ang)
+    xc = torch.view_as_complex(T(x).reshape(L, H, d // 2, 2).contiguous())
+    return torch.view_as_real(xc * rot[:, None, :]).reshape(L, H, d).numpy()
+
+
+def test_rope_matches_complex_rotation():
+    r = np.random.default_rng(6)
+    x = r.standard_normal((24, 2, 64))
+    pos = oracle.token_positions(5, (2, 3, 4))
+    np.testing.assert_allclose(oracle.rope3d(x, pos), _rope_complex(x, pos), rtol=1e-12, atol=1e-12)
+
+
+def test_rope_invariants():
+    r = np.random.default_rng(7)
+    x = r.standard_normal((1, 1, 128))
+    zero = np.zeros((1, 3), dtype=np.int64)
+    np.testing.assert_array_equal(oracle.rope3d(x, zero), x)
+    p = np.array([[7, 3, 11]])
+    y = oracle.rope3d(x, p)
+    # norm of every rotated pair is preserved
+    np.testing.assert_allclose((y.reshape(64, 2) ** 2).sum(1), (x.reshape(64, 2) ** 2).sum(1), rtol=1e-12)
+    # a row-only position moves only the middle segment
+    y = oracle.rope3d(x, np.array([[0, 5, 0]]))
+    np.testing.assert_array_equal(y[..., :44], x[..., :44])
+    np.testing.assert_array_equal(y[..., 86:], x[..., 86:])
+    assert not np.allclose(y[..., 44:86], x[..., 44:86])
+    # relative property: <R(p) q, R(p') k> depends on p - p' only
+    q = r.standard_normal((1, 1, 128))
+    k = r.standard_normal((1, 1, 128))
+    a = (oracle.rope3d(q, np.array([[9, 4, 2]])) * oracle.rope3d(k, np.array([[6, 1, 7]]))).sum()
+    b = (oracle.rope3d(q, np.array([[3, 3, 0]])) * oracle.rope3d(k, np.array([[0, 0, 5]]))).sum()
+    assert abs(a - b) < 1e-10
+
+
+# ---------------------------------------------------------------- the whole block
+def _torch_block(h, e, w, chunk, prior, ctx, grid, H):
+    """An independent statement of the block with torch library routines."""
+    L, D = h.shape
+    d = D // H
+    mod = T(e) + T(w["tmod"])
+    shift1, scale1, gate1, shift2, scale2, gate2 = mod
+    x = T(h)
+    y = F.layer_norm(x, (D,), eps=1e-6) * (1 + scale1) + shift1
+    qkv = F.linear(y, T(w["wqkv"]).T, T(w["bqkv"]))
+    q, k, v = [t.reshape(L, H, d) for t in qkv.split(D, dim=1)]
+    pos = oracle.token_positions(chunk, grid)
+    q = T(_rope_complex(q.numpy(), pos))
+    k = T(_rope_complex(k.numpy(), pos))
+    K = torch.cat([T(p[0]) for p in prior] + [k])
+    V = torch.cat([T(p[1]) for p in prior] + [v])
+    a = F.scaled_dot_product_attention(q.transpose(0, 1), K.transpose(0, 1), V.transpose(0, 1))
+    x = x + gate1 * F.linear(a.transpose(0, 1).reshape(L, D), T(w["wo"]).T, T(w["bo"]))
+    q2 = F.linear(F.layer_norm(x, (D,), eps=1e-6), T(w["wq2"]).T, T(w["bq2"])).reshape(L, H, d)
+    kv2 = F.linear(T(ctx), T(w["wkv2"]).T, T(w["bkv2"]))
+    k2, v2 = [t.reshape(-1, H, d) for t in kv2.split(D, dim=1)]
+    a2 = F.scaled_dot_product_attention(q2.transpose(0, 1), k2.transpose(0, 1), v2.transpose(0, 1))
+    x = x + F.linear(a2.transpose(0, 1).reshape(L, D), T(w["wo2"]).T, T(w["bo2"]))
+    y3 = F.layer_norm(x, (D,), eps=1e-6) * (1 + scale2) + shift2
+    f = F.gelu(F.linear(y3, T(w["w1"]).T, T(w["b1"])), approximate="tanh")
+    x = x + gate2 * F.linear(f, T(w["w2"]).T, T(w["b2"]))
+    return x.numpy(), k.numpy(), v.numpy()
+
+
+def _small_cfg():
+    return with_(C1, hidden=64, heads=2, head_dim=32, ffn=96, grid=(2, 2, 3), n_ctx=5)
+
+
+def _scaled_weights(cfg, seed):
+    w = inputs.block_weights(cfg, 0, seed)
+    # larger weights than the workloads use so every branch moves h visibly
+    return {k: v * (10.0 if k != "tmod" else 40.0) for k, v in w.items()}
+
+
+def test_block_matches_library_composition():
+    cfg = _small_cfg()
+    r = np.random.default_rng(8)
+    w = _scaled_weights(cfg, 3)
+    L, D, H, d = cfg.tokens, cfg.hidden, cfg.heads, cfg.head_dim
+    h = r.standard_normal((L, D))
+    e = r.standard_normal((6, D))
+    prior = [(r.standard_normal((L, H, d)), r.standard_normal((L, H, d))) for _ in range(2)]
+    ctx = r.standard_normal((cfg.n_ctx, D))
+    ck = oracle.context_kv(ctx, w, H)
+    got, (k, v) = oracle.block_task(h, e, w, 4, prior, ck, cfg.grid, H)
+    ref, rk, rv = _torch_block(h, e, w, 4, prior, ctx, cfg.grid, H)
+    np.testing.assert_allclose(k, rk, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(v, rv, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+    assert np.abs(got - h).max() > 0.1  # the branches did something
+
+
+def test_block_rows_subset_equals_full():
+    cfg = _small_cfg()
+    r = np.random.default_rng(9)
+    w = _scaled_weights(cfg, 4)
+    L, D, H, d = cfg.tokens, cfg.hidden, cfg.heads, cfg.head_dim
+    h = r.standard_normal((L, D))
+    e = r.standard_normal((6, D))
+    ck = oracle.context_kv(r.standard_normal((cfg.n_ctx, D)), w, H)
+    prior = [(r.standard_normal((L, H, d)), r.standard_normal((L, H, d)))]
+    full, _ = oracle.block_task(h, e, w, 1, prior, ck, cfg.grid, H)
+    rows = np.array([0, 5, L - 1])
+    part, _ = oracle.block_task(h, e, w, 1, prior, ck, cfg.grid, H, rows=rows)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-13, atol=1e-13)
+
+
+def test_block_identity_with_zero_gates():
+    """gate1 = gate2 = 0 and a zero cross branch leave h unchanged exactly."""
+    cfg = _small_cfg()
+    r = np.random.default_rng(10)
+    w = _scaled_weights(cfg, 5)
+    w["wo2"] = np.zeros_like(w["wo2"])
+    w["bo2"] = np.zeros_like(w["bo2"])
+    L, D, H = cfg.tokens, cfg.hidden, cfg.heads
+    e = r.standard_normal((6, D))
+    w["tmod"] = w["tmod"].astype(np.float64)
+    w["tmod"][2] = -e[2]
+    w["tmod"][5] = -e[5]
+    h = r.standard_normal((L, D))
+    ck = oracle.context_kv(r.standard_normal((cfg.n_ctx, D)), w, H)
+    out, _ = oracle.block_task(h, e, w, 0, [], ck, cfg.grid, H)
+    np.testing.assert_array_equal(out, h)
