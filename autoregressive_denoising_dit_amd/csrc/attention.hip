@@ -1,0 +1,254 @@
+// Flash-style attention of a stage task over its noisy-KV window (gfx950).
+//
+// Self-attention: chunk c at step s attends to the keys/values that chunks
+// c - n_read .. c - 1 left at the same (block, step) -- still noisy -- and to
+// its own (AREX article on the PhysisServe report, section "难题"; 163.com
+// release, section "新一代物理 AI 的基础设施", Fig. 1).  Those entries sit in
+// ring slots of the pool, so the key sequence is a list of segments (read
+// slots oldest first, then the write slot).  Cross-attention uses the same
+// kernel with one segment, the stream's cached conditioning keys/values.
+//
+// Formulation: the kernel computes S^T = K Q^T and O^T = V^T P^T with MFMA
+// 32x32 tiles.  In the accumulator layout a lane then holds one query (its
+// column) and several keys, so (i) the softmax row statistics are lane-local
+// plus one exchange between the two half-waves, (ii) rescaling O^T by the
+// running max touches only the lane's own registers, and (iii) the
+// probabilities P^T are already in the B-operand layout of the next MFMA --
+// no LDS round trip for P.  V is stored transposed in the pool (V^T [d][L])
+// so that P V contracts along contiguous memory.
+//
+// Work split: one workgroup = (128-query tile, head, task); 4 waves x 32
+// queries.  Keys stream through LDS in 64-key tiles, double-buffered, with
+// the next tile fetched into registers while the current one is used.
+// Softmax runs in fp32 with exp2 on logits pre-scaled by log2(e)/sqrt(d)
+// (the scale is folded into q by the producing GEMM).
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ps {
+
+namespace {
+
+constexpr int NT = 256, QT = 128, KT = 64;
+
+template <typename T, int HD>
+__global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restrict__ out,
+                                             PoolGeo pg, const DevTask* __restrict__ tasks, int cross) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int KCH = HD / VEC;     // 16-byte chunks per K row
+  constexpr int VCH = KT / VEC;     // 16-byte chunks per V^T row
+  constexpr int NU_QK = KCH / 2;    // k-units of the QK contraction
+  constexpr int NU_PV = VCH / 2;    // k-units of the PV contraction
+  constexpr int KLD = KT * KCH / NT;   // K chunks per thread per tile
+  constexpr int VLD = HD * VCH / NT;   // V chunks per thread per tile
+  constexpr bool kBf16 = sizeof(T) == 2;
+  __shared__ u32x4 ks[2][KT * KCH];
+  __shared__ u32x4 vs[2][HD * VCH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int h = blockIdx.y, task = blockIdx.z;
+  const DevTask& tk = tasks[task];
+  const int L = pg.L, D = pg.H * HD;
+
+  // key segments
+  int n_seg, seg_valid, seg_stride;
+  if (cross) {
+    n_seg = 1; seg_valid = tk.ctx_len; seg_stride = pg.max_ctx;
+  } else {
+    n_seg = tk.n_seg; seg_valid = L; seg_stride = L;
+  }
+  const int n_keys = n_seg * seg_valid;
+  auto seg_base = [&](int sgi) -> const T* {
+    if (cross) return static_cast<const T*>(pg.ctx) + (size_t)tk.ctx_region * pg.ctx_elems;
+    return static_cast<const T*>(pg.kv) +
+           ((size_t)tk.region * pg.n_slots + tk.slots[sgi]) * pg.slot_elems;
+  };
+  const size_t v_off = (size_t)pg.H * seg_stride * HD;
+
+  // this lane's query and its Q fragments (B operand of S^T = K Q^T)
+  const int qi = blockIdx.x * QT + wave * 32 + l32;
+  const int qc = min(qi, L - 1);
+  const T* qrow = q + ((size_t)task * L + qc) * D + (size_t)h * HD;
+  u32x4 qf[NU_QK];
+#pragma unroll
+  for (int u = 0; u < NU_QK; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + (2 * u + g) * VEC);
+
+  // per-thread load slots
+  u32x4 kr[KLD], vr[VLD];
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int e = tid + NT * i;
+      const int row = e / KCH, c = e % KCH;
+      const int j = min(tile * KT + row, n_keys - 1);
+      const int sgi = j / seg_valid, tok = j - sgi * seg_valid;
+      kr[i] = *reinterpret_cast<const u32x4*>(seg_base(sgi) + ((size_t)h * seg_stride + tok) * HD +
+                                              c * VEC);
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int e = tid + NT * i;
+      const int f = e / VCH, c = e % VCH;
+      const int j0 = min(tile * KT + c * VEC, n_keys - VEC);
+      const int sgi = j0 / seg_valid, tok = j0 - sgi * seg_valid;
+      vr[i] = *reinterpret_cast<const u32x4*>(seg_base(sgi) + v_off +
+                                              ((size_t)h * HD + f) * seg_stride + tok);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int e = tid + NT * i;
+      const int row = e / KCH, c = e % KCH;
+      ks[buf][row * KCH + (c ^ (row & 7))] = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+      const int e = tid + NT * i;
+      const int f = e / VCH, c = e % VCH;
+      if constexpr (kBf16) {
+        // keys of a 16-key group are kept in the order {0-3, 8-11, 4-7, 12-15}
+        // so that half-wave g reads its 8 keys {4g..4g+3, 8+4g..8+4g+3} as one
+        // 16-byte chunk, matching the probabilities it holds.
+        const int grp = c >> 1, half = c & 1;
+        u32x2* lo = reinterpret_cast<u32x2*>(&vs[buf][f * VCH + ((2 * grp) ^ (f & 7))]);
+        u32x2* hi = reinterpret_cast<u32x2*>(&vs[buf][f * VCH + ((2 * grp + 1) ^ (f & 7))]);
+        lo[half] = u32x2{vr[i].x, vr[i].y};
+        hi[half] = u32x2{vr[i].z, vr[i].w};
+      } else {
+        vs[buf][f * VCH + (c ^ (f & 7))] = vr[i];
+      }
+    }
+  };
+
+  f32x16 o[HD / 32];
+#pragma unroll
+  for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int n_tiles = (n_keys + KT - 1) / KT;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < n_tiles) fetch(tile + 1);
+
+    // S^T for the 64 keys of this tile: two 32-key row tiles
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < NU_QK; ++u) {
+        const u32x4 kf = ks[buf][(t * 32 + l32) * KCH + ((2 * u + g) ^ (l32 & 7))];
+        Mfma<T>::unit(s[t], kf, qf[u]);
+      }
+    }
+    // mask keys past the end, then the online softmax update
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = tile * KT + t * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+        if (key >= n_keys) s[t][r] = -INFINITY;
+        mloc = fmaxf(mloc, s[t][r]);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[t][r] = exp2f(s[t][r] - m_new);
+        psum += s[t][r];
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int u = 0; u < NU_PV; ++u) {
+      u32x4 pf;
+      if constexpr (kBf16) {
+        const int t = u >> 1, r0 = (u & 1) * 8;
+        bf16x8 pb;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) pb[r] = (bf16)s[t][r0 + r];
+        pf = __builtin_bit_cast(u32x4, pb);
+      } else {
+        const int t = u >> 2, r0 = (u & 3) * 4;
+        pf = u32x4{__builtin_bit_cast(uint32_t, s[t][r0]), __builtin_bit_cast(uint32_t, s[t][r0 + 1]),
+                   __builtin_bit_cast(uint32_t, s[t][r0 + 2]), __builtin_bit_cast(uint32_t, s[t][r0 + 3])};
+      }
+#pragma unroll
+      for (int i = 0; i < HD / 32; ++i) {
+        const int f = i * 32 + l32;
+        const u32x4 vf = vs[buf][f * VCH + ((2 * u + g) ^ (f & 7))];
+        Mfma<T>::unit(o[i], vf, pf);
+      }
+    }
+
+    if (tile + 1 < n_tiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  if (qi < L) {
+    T* orow = out + ((size_t)task * L + qi) * D + (size_t)h * HD;
+#pragma unroll
+    for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int f = i * 32 + rg * 8 + g * 4;
+        if constexpr (kBf16) {
+          bf16x4 w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = (bf16)(o[i][rg * 4 + r] * inv);
+          *reinterpret_cast<bf16x4*>(orow + f) = w;
+        } else {
+          f32x4 w;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = o[i][rg * 4 + r] * inv;
+          *reinterpret_cast<f32x4*>(orow + f) = w;
+        }
+      }
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_attention(bool cross, const T* q, T* out, const PoolGeo& pg, const DevTask* tt,
+                            int n_tasks, hipStream_t s) {
+  dim3 grid((pg.L + QT - 1) / QT, pg.H, n_tasks), block(NT);
+  if (pg.d == 128) {
+    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, q, out, pg, tt, cross ? 1 : 0);
+  } else if (pg.d == 64) {
+    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, q, out, pg, tt, cross ? 1 : 0);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_attention<bf16>(bool, const bf16*, bf16*, const PoolGeo&, const DevTask*,
+                                           int, hipStream_t);
+template hipError_t launch_attention<float>(bool, const float*, float*, const PoolGeo&,
+                                            const DevTask*, int, hipStream_t);
+
+}  // namespace ps

@@ -1,0 +1,112 @@
+// Internal types shared by the gfx950 kernels and the C-ABI layer of libps.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ps.h"
+
+namespace ps {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// --------------------------------------------------------------------------
+// MFMA building block.  A "k-unit" is one 16-byte chunk per lane from each
+// operand (lanes 0-31 and 32-63 supply different chunks).  For bf16 that is
+// one v_mfma_f32_32x32x16_bf16 (16 k values); for fp32 four
+// v_mfma_f32_32x32x2_f32 (8 k values).  A and B use the same k order, so any
+// permutation of k inside the unit gives the same product.
+//
+// Output layout of a 32x32 accumulator (f32x16 per lane): lane l holds column
+// l % 32 and rows 8 * (r / 4) + 4 * (l / 32) + (r % 4), r = 0..15.
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<bf16> {
+  static constexpr int kPerUnit = 16;
+  __device__ __forceinline__ static void unit(f32x16& acc, u32x4 a, u32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<float> {
+  static constexpr int kPerUnit = 8;
+  __device__ __forceinline__ static void unit(f32x16& acc, u32x4 a, u32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.x),
+                                               __builtin_bit_cast(float, b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.y),
+                                               __builtin_bit_cast(float, b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.z),
+                                               __builtin_bit_cast(float, b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.w),
+                                               __builtin_bit_cast(float, b.w), acc, 0, 0, 0);
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) { return (float)x; }
+
+// --------------------------------------------------------------------------
+// Stage tasks as the kernels see them (passed by value as a kernel argument).
+struct DevTask {
+  int32_t region;       // ((stream * n_blocks) + block) * n_steps + step
+  int32_t ctx_region;   // stream * n_blocks + block
+  int32_t chunk;
+  int32_t n_seg;        // n_read + 1 chunks of keys
+  int32_t ctx_len;      // conditioning tokens of the stream
+  int32_t slots[PS_MAX_WINDOW + 1];  // read slots (oldest first), then the write slot
+};
+
+// Host-side image of the batch's task list; it travels to device memory as
+// the argument of a one-thread copy kernel (stream-ordered, no host staging).
+struct TaskTable {
+  DevTask t[PS_MAX_TASKS];
+  int32_t n;
+};
+
+// Division by a runtime-constant divisor d (n < 2^31):
+// q = (umulhi(n, mul) + n) >> shift with shift = ceil(log2 d) and
+// mul = floor(2^32 (2^shift - d) / d) + 1.
+struct FastDiv {
+  uint32_t d = 1, mul = 1, shift = 0;
+  FastDiv() = default;
+  explicit FastDiv(uint32_t div) : d(div) {
+    shift = 0;
+    while ((1ull << shift) < div) ++shift;
+    mul = (uint32_t)(((1ull << 32) * ((1ull << shift) - div)) / div + 1);
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const { return (__umulhi(n, mul) + n) >> shift; }
+};
+
+// Pool geometry.  Slot layout: K [H][L][d] then V^T [H][d][L].  Context
+// layout per (stream, block): K [H][Lc][d] then V^T [H][d][Lc], Lc = max_ctx.
+struct PoolGeo {
+  void* kv;
+  void* ctx;
+  int64_t slot_elems;
+  int64_t ctx_elems;
+  int32_t n_slots, L, H, d, max_ctx;
+  int32_t frames, rows, cols;
+  int32_t seg_f, seg_h, seg_w;     // RoPE segments of the head dim
+  const float2* rope_y;            // [rows][seg_h / 2] (cos, sin)
+  const float2* rope_x;            // [cols][seg_w / 2]
+  FastDiv div_L, div_plane, div_cols, div_rows;  // L, rows * cols, cols, rows
+};
+
+}  // namespace ps

@@ -1,0 +1,92 @@
+"""Host driver of the staggered chunk x step schedule on one GPU.
+
+Each chunk starts from noise and passes S denoising steps; chunk c + 1 does not
+wait for chunk c to finish -- it reads the noisy KV chunk c left at the same
+step, so adjacent chunks' denoising is offset and overlaps (AREX feed article
+on the PhysisServe report, section "难题"; 163.com release, section
+"新一代物理 AI 的基础设施", Fig. 1).  One GPU time-shares all stages and, per
+block, batches the tasks of different chunks and steps (AREX article,
+"三层设计", layer 2; 163.com release, bullet "时分复用").
+
+Tick tau holds the tasks (stream, c, s) with c = k (tau - s) + j, 0 <= j < k.
+For each block b the tick's tasks form one ps_stage_batch call; after the last
+block every task takes its Euler step.  Tasks are ordered by chunk, then
+stream, so that with latents stored chunk-major the tick's rows are one
+contiguous slice: the first block reads the latents in place and the Euler
+step updates them in place -- no gather or scatter copies.
+
+Ring slots: chunk c uses slot c mod R of its (stream, block, step), R >= W + k;
+it reads the slots of chunks max(0, c - W) .. c - 1 (fewer while c < W).
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import runtime
+from .runtime import Block, Pool, TimeEmbed
+
+
+def tick_tasks(tau: int, n_chunks: int, n_steps: int, k: int, n_streams: int) -> List[Tuple[int, int, int]]:
+    """(stream, chunk, step) of tick tau, ordered by chunk then stream."""
+    out = []
+    for s in range(n_steps - 1, -1, -1):          # older chunks (later steps) first
+        for j in range(k):
+            c = k * (tau - s) + j
+            if 0 <= c < n_chunks:
+                for sg in range(n_streams):
+                    out.append((sg, c, s))
+    out.sort(key=lambda t: (t[1], t[0]))
+    return out
+
+
+def n_ticks(n_chunks: int, n_steps: int, k: int) -> int:
+    return math.ceil(n_chunks / k) + n_steps - 1
+
+
+class StaggeredRunner:
+    """Runs the staggered schedule of `n_chunks` chunks of `n_streams` streams."""
+
+    def __init__(self, pool: Pool, blocks: Sequence[Block], te: TimeEmbed, timesteps: Sequence[float],
+                 window: int, k: int, n_streams: int):
+        if pool.n_slots < window + k:
+            raise ValueError(f"ring of {pool.n_slots} slots is smaller than window + k = {window + k}")
+        self.pool, self.blocks, self.te = pool, list(blocks), te
+        self.ts = list(timesteps) + [0.0]
+        self.S, self.W, self.k, self.n_streams = len(timesteps), window, k, n_streams
+        self.L, self.D = pool.tokens, pool.hidden
+        self.hbuf = torch.empty((self.S * k * n_streams * self.L, self.D), dtype=torch.float32, device="cuda")
+
+    def tasks_for(self, tau: int, n_chunks: int):
+        tl = tick_tasks(tau, n_chunks, self.S, self.k, self.n_streams)
+        R = self.pool.n_slots
+        ps_tasks = []
+        for (sg, c, s) in tl:
+            nr = min(self.W, c)
+            ps_tasks.append(runtime.make_task(sg, c, s, self.ts[s], c % R,
+                                              [(c - nr + i) % R for i in range(nr)]))
+        return tl, ps_tasks
+
+    def run_tick(self, tau: int, x: torch.Tensor, n_chunks: int):
+        """x: fp32 [n_chunks, n_streams, L, D] latents (updated in place)."""
+        tl, tasks = self.tasks_for(tau, n_chunks)
+        if not tl:
+            return tl
+        c_lo = tl[0][1]
+        n = len(tl)
+        rows = n * self.L
+        xs = x[c_lo:c_lo + n // self.n_streams].view(rows, self.D)
+        h = self.hbuf[:rows]
+        for b, blk in enumerate(self.blocks):
+            runtime.stage_batch(self.pool, blk, self.te, tasks, xs if b == 0 else h, h)
+        dts = [self.ts[s] - self.ts[s + 1] for (_, _, s) in tl]
+        runtime.euler_update(xs, h, dts, self.L, self.D)
+        return tl
+
+    def run(self, x: torch.Tensor, n_chunks: int, on_tick: Optional[Callable[[int, list], None]] = None):
+        for tau in range(n_ticks(n_chunks, self.S, self.k)):
+            tl = self.run_tick(tau, x, n_chunks)
+            if on_tick is not None:
+                on_tick(tau, tl)

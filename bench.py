@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Stage-task throughput on one MI355X (gfx950).
+
+A step is one pass of the whole stage path over one batch of synthetic input:
+batch formation, per-task modulation, AdaLN + QKV + 3D RoPE + cache write,
+self-attention over the noisy-KV window, gated O projection, cross-attention,
+the gated GELU-tanh FFN, and the flow-matching Euler update of the batch's
+latents.  Default workload: the Wan2.1-14B-shaped stage, 16 tasks from 16
+streams at mixed denoising steps per batch (hidden 5120, 40 x 128 heads, FFN
+13824, 1560 tokens per chunk, window of 3 prior chunks, 512 conditioning
+tokens, bf16 operands).  Weights are random-init of that shape (no trained
+weights are available), inputs seeded, everything resident in HBM before the
+timed region starts.
+
+Prints one JSON line: stage tasks/s, ms per step, the steady-state chunk
+interval, the fraction of the bf16 MFMA peak, a roofline record of the
+dominant kernel (HIP-event timing inside the timed region) and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK = {"bf16": 2516.6e12, "fp32": 157.3e12}   # dense MFMA, 256 CU x 2.4 GHz
+HBM_PEAK = 8.0e12
+
+
+def _log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_work(cfg, n_tasks, n_read):
+    """Algorithmic FLOPs (contractions) or bytes (memory-bound kernels) per launch."""
+    L, D, F, Lc = cfg.tokens, cfg.hidden, cfg.ffn, cfg.n_ctx
+    M = n_tasks * L
+    es = 2 if cfg.dtype == "bf16" else 4
+    return {
+        "qkv": ("flop", 2 * M * D * 3 * D),
+        "attn_self": ("flop", 4 * L * (n_read + 1) * L * D * n_tasks),
+        "o_proj": ("flop", 2 * M * D * D),
+        "xq_proj": ("flop", 2 * M * D * D),
+        "attn_cross": ("flop", 4 * L * Lc * D * n_tasks),
+        "xo_proj": ("flop", 2 * M * D * D),
+        "ffn1": ("flop", 2 * M * D * F),
+        "ffn2": ("flop", 2 * M * F * D),
+        "ln1": ("byte", M * D * (4 + es)),
+        "ln2": ("byte", M * D * (4 + es)),
+        "ln3": ("byte", M * D * (4 + es)),
+        "euler": ("byte", M * D * 12),
+    }
+
+
+def setup_stage(cfg, n_tasks, seed=0):
+    """Device-resident weights, pool, contexts and inputs for single-stage runs."""
+    import torch
+    from autoregressive_denoising_dit_amd import runtime
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    D, F, H, d = cfg.hidden, cfg.ffn, cfg.heads, cfg.head_dim
+
+    def rn(*shape, dtype=torch.float32, std=0.02):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(dtype).contiguous()
+
+    w = {"wqkv": rn(3 * D, D, dtype=td), "wo": rn(D, D, dtype=td), "wq2": rn(D, D, dtype=td),
+         "wkv2": rn(2 * D, D, dtype=td), "wo2": rn(D, D, dtype=td), "w1": rn(F, D, dtype=td),
+         "w2": rn(D, F, dtype=td), "bqkv": rn(3 * D), "bo": rn(D), "bq2": rn(D), "bkv2": rn(2 * D),
+         "bo2": rn(D), "b1": rn(F), "b2": rn(D), "tmod": rn(6, D)}
+    tw = {"wt1": rn(D, 256), "bt1": rn(D), "wt2": rn(D, D), "bt2": rn(D), "wp": rn(6 * D, D), "bp": rn(6 * D)}
+    n_streams = n_tasks
+    R = cfg.window + 1
+    pool = runtime.Pool(n_streams, 1, cfg.n_steps, R, cfg.grid, H, d, cfg.n_ctx, runtime.ps_dtype(cfg.dtype))
+    blk = runtime.Block(w, D, H, d, F, 0, runtime.ps_dtype(cfg.dtype))
+    te = runtime.TimeEmbed(tw, D, capacity=16)
+    kv_k = rn(cfg.tokens, H, d, dtype=td, std=1.0)
+    kv_v = rn(cfg.tokens, H, d, dtype=td, std=1.0)
+    for sg in range(n_streams):
+        pool.context_set(blk, sg, rn(cfg.n_ctx, D, dtype=td, std=1.0))
+        for s in range(cfg.n_steps):
+            for slot in range(R):
+                pool.load(sg, 0, s, slot, 0, kv_k, kv_v)
+    x = rn(n_tasks * cfg.tokens, D, std=1.0)
+    h = torch.empty_like(x)
+    xe = x.clone()
+    torch.cuda.synchronize()
+    return dict(pool=pool, blk=blk, te=te, x=x, h=h, xe=xe, w=w, tw=tw)
+
+
+def stage_tasks(cfg, n_tasks, tau, base_chunk=100):
+    """Task i: stream i at step (tau + i) mod S, a steady-state chunk with a full window."""
+    from autoregressive_denoising_dit_amd import runtime
+    R = cfg.window + 1
+    out = []
+    for i in range(n_tasks):
+        s = (tau + i) % cfg.n_steps
+        c = base_chunk + tau
+        out.append(runtime.make_task(i, c, s, cfg.timesteps[s], c % R,
+                                     [(c - cfg.window + j) % R for j in range(cfg.window)]))
+    return out
+
+
+def run_stage_bench(cfg, n_tasks, steps, warmup):
+    import torch
+    from autoregressive_denoising_dit_amd import _lib, runtime
+    _log(f"setting up {cfg.name}: {n_tasks} tasks per batch")
+    st = setup_stage(cfg, n_tasks)
+    L, D = cfg.tokens, cfg.hidden
+    task_lists = [stage_tasks(cfg, n_tasks, tau) for tau in range(cfg.n_steps)]
+    dts = [[cfg.timesteps[t.step] - (cfg.timesteps[t.step + 1] if t.step + 1 < cfg.n_steps else 0.0)
+            for t in tl] for tl in task_lists]
+
+    def step(tau):
+        tl = task_lists[tau % cfg.n_steps]
+        runtime.stage_batch(st["pool"], st["blk"], st["te"], tl, st["x"], st["h"])
+        runtime.euler_update(st["xe"], st["h"], dts[tau % cfg.n_steps], L, D)
+
+    for tau in range(warmup):
+        step(tau)
+    torch.cuda.synchronize()
+    _lib.trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for tau in range(steps):
+        step(tau)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    trace = _lib.trace_read()
+    _lib.trace_enable(False)
+    assert torch.isfinite(st["h"]).all().item(), "non-finite stage output"
+    sec = (t1 - t0) / steps
+    return sec, trace
+
+
+def cpu_baseline(cfg, n_read, budget_s=30.0):
+    """The float64 CPU oracle on one task of the workload (a bounded sample)."""
+    import numpy as np
+    import oracle
+    from synthetic import inputs, stage_flops
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    _log("cpu baseline: generating one block's weights")
+    w = inputs.block_weights(cfg, 0, 0)
+    tw = inputs.time_weights(cfg, 0)
+    L, H, d = cfg.tokens, cfg.heads, cfg.head_dim
+    h = inputs.hidden_rows(cfg, 1, 0)
+    prior = [inputs.cache_entry(cfg, 0, 0, 0, j, 0) for j in range(n_read)]
+    ctx_kv = oracle.context_kv(inputs.context(cfg, 0, 0), w, H)
+    e = oracle.time_embedding(cfg.timesteps[0], tw)
+    # sample: all rows through the QKV phase (every key/value is needed), then
+    # the rest of the block for a subset of query rows; scaled by FLOPs
+    frac = 0.25
+    rows = np.arange(0, L, int(round(1 / frac)))
+    _log(f"cpu baseline: oracle stage task, {len(rows)} of {L} query rows")
+    t0 = time.perf_counter()
+    oracle.block_task(h, e, w, 10, prior, ctx_kv, cfg.grid, H, rows=rows)
+    dt = time.perf_counter() - t0
+    full = stage_flops(cfg, n_read)
+    qkv = 2 * L * cfg.hidden * 3 * cfg.hidden
+    sample = qkv + (full - qkv) * len(rows) / L
+    task_s = dt * full / sample
+    return {"value": 1.0 / task_s, "unit": "tasks/s", "cores": threads, "kind": "oracle",
+            "sample": f"one {cfg.name} stage task in float64 NumPy: QKV phase over all {L} tokens, "
+                      f"the rest of the block for {len(rows)} query rows; {dt:.1f} s measured, "
+                      f"scaled by algorithmic FLOPs to a whole task ({task_s:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5", choices=["c2", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synthetic import get, stage_flops
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cfg = get(args.workload)
+    n_tasks = cfg.batch
+    n_read = cfg.window
+    sec, trace = run_stage_bench(cfg, n_tasks, args.steps, args.warmup)
+    flops_step = n_tasks * stage_flops(cfg, n_read)
+    peak = PEAK[cfg.dtype]
+    work = kernel_work(cfg, n_tasks, n_read)
+    kernels = {}
+    for name, (launches, ms) in trace.items():
+        avg_ms = ms / max(launches, 1)
+        rec = {"launches": launches, "avg_ms": round(avg_ms, 4)}
+        if name in work:
+            kind, amount = work[name]
+            if kind == "flop":
+                rec["tflops"] = round(amount / (avg_ms * 1e-3) / 1e12, 1)
+            else:
+                rec["gbs"] = round(amount / (avg_ms * 1e-3) / 1e9, 1)
+        kernels[name] = rec
+    dom = max((n for n in trace if n in work), key=lambda n: trace[n][1])
+    kind, amount = work[dom]
+    avg_s = trace[dom][1] / trace[dom][0] * 1e-3
+    if kind == "flop":
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(amount / avg_s / 1e12, 2), "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": round(amount / avg_s / peak, 4), "traffic": None}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / avg_s / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": round(amount / avg_s / HBM_PEAK, 4), "traffic": None}
+    out = {
+        "metric": "stage tasks/sec + steady-state chunk interval (ms) on 1 MI355X; % MFMA peak",
+        "value": round(n_tasks / sec, 2),
+        "unit": "tasks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded random-init weights, N(0,1) latents, contexts and pre-filled noisy KV)",
+        "config": {"workload": cfg.name, "tasks_per_batch": n_tasks, "tokens_per_chunk": cfg.tokens,
+                   "hidden": cfg.hidden, "heads": cfg.heads, "head_dim": cfg.head_dim, "ffn": cfg.ffn,
+                   "window": cfg.window, "ctx_tokens": cfg.n_ctx, "steps_mixed": cfg.n_steps},
+        # each stream's chunk needs one task per denoising step at this block
+        "chunk_interval_ms": round(sec * 1e3 * cfg.n_steps, 3),
+        "mfma_frac": round(flops_step / sec / peak, 4),
+        "stage_tflops": round(flops_step / sec / 1e12, 1),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, n_read)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

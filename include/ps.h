@@ -1,0 +1,226 @@
+/*
+ * ps.h -- C ABI of libps: the stage task of an autoregressive-denoising DiT
+ * server, on one AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute.  A *stage* is one Transformer block at one denoising
+ * step, and it is the unit of compute allocation (AREX feed article on the
+ * PhysisServe report, section "三层设计", layer 1; 163.com release, section
+ * "PhysisServe", bullet "Stage-wise 流水线").  Chunk c at step s reads the
+ * still-noisy KV cache that earlier chunks left at that same step (AREX article,
+ * section "难题"; 163.com release, section "新一代物理 AI 的基础设施", Fig. 1).
+ * One GPU runs tasks of several stages in time slices and batches tasks of the
+ * same block from different chunks and denoising steps against that block's
+ * weights (AREX article, "三层设计", layer 2; 163.com release, bullet "时分复用",
+ * Fig. 3; aicoder news, "Time-Shared Multi-Request Batching").
+ *
+ * Conventions for every call.
+ *  - Return value: PS_OK (0) or a negative ps_status.  On failure nothing has
+ *    been enqueued on the stream and ps_last_error() holds a message.
+ *  - Arguments are validated on the host before any launch.  Calls that take a
+ *    hipStream_t are asynchronous in that stream's order; a device fault shows
+ *    up as PS_ERR_HIP on a later call.
+ *  - Pointers named "device" must be device memory of the current HIP device;
+ *    "host" pointers are read before the call returns.  The caller owns every
+ *    tensor pointer it passes; the library owns handles, the KV pool, the
+ *    cached timestep embeddings and the internal workspace.
+ *  - Handles are not thread-safe.  One handle is used from one host thread, and
+ *    the calls that share a handle must be ordered on one stream.
+ *  - Element types: ps_dtype PS_BF16 (bfloat16) or PS_F32.  "compute dtype"
+ *    means the dtype of the pool/block.  The residual stream (h) and the
+ *    latents (x) are always fp32; biases, modulation tables and the timestep
+ *    MLP are fp32.
+ */
+#ifndef PS_H_
+#define PS_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ps_status;
+#define PS_OK 0
+#define PS_ERR_INVALID_ARG (-1)
+#define PS_ERR_OUT_OF_MEMORY (-2)
+#define PS_ERR_HIP (-3)
+#define PS_ERR_SLOT_CONFLICT (-4)
+#define PS_ERR_UNSUPPORTED (-5)
+
+typedef int32_t ps_dtype;
+#define PS_F32 0
+#define PS_BF16 1
+
+#define PS_MAX_WINDOW 8   /* most prior chunks one task may read */
+#define PS_MAX_TASKS 32   /* most tasks in one ps_stage_batch call */
+#define PS_FREQ_DIM 256   /* sinusoidal timestep features */
+
+typedef struct ps_kv_pool ps_kv_pool;
+typedef struct ps_block ps_block;
+typedef struct ps_time_embed ps_time_embed;
+
+/* ------------------------------------------------------------------ pool --
+ * The noisy-KV pool: for every (stream, block, step) a ring of n_slots slots,
+ * each holding one chunk's keys (after 3D RoPE) and values in the compute
+ * dtype.  Chunk c at a step reads the entries of earlier chunks at that same
+ * (block, step) (AREX article, "难题"; 163.com release, Fig. 1); the KV never
+ * leaves the GPU that computed it (AREX article, "三层设计", layer 1).
+ * Which slot a chunk uses is the caller's choice (ps_task); a ring of
+ * window + k slots suffices for a schedule that admits k chunks per step per
+ * tick.  The pool also holds, per (stream, block), the cross-attention keys
+ * and values of that stream's conditioning tokens (ps_context_set).
+ *
+ * Token grid: a chunk has L = frames * rows * cols tokens, row-major
+ * (token n = (f * rows + y) * cols + x); its frame coordinate for RoPE is
+ * chunk * frames + f.  L must be a multiple of 8 and n_ctx a multiple of 8.
+ * head_dim must be 64 or 128.  check_slots = 1 turns on the slot ledger:
+ * each slot remembers which chunk wrote it, and ps_stage_batch rejects a task
+ * whose read slots do not hold chunks c - n_read .. c - 1
+ * (PS_ERR_SLOT_CONFLICT, nothing launched).
+ */
+typedef struct {
+  int32_t n_streams, n_blocks, n_steps, n_slots;
+  int32_t frames, rows, cols;
+  int32_t n_heads, head_dim;
+  int32_t max_ctx;          /* most conditioning tokens per stream */
+  ps_dtype dtype;
+  int32_t check_slots;
+} ps_pool_desc;
+
+/* Allocates the pool (device memory, uninitialised) and its RoPE tables.
+ * Errors: PS_ERR_INVALID_ARG (bad sizes), PS_ERR_OUT_OF_MEMORY, PS_ERR_HIP. */
+ps_status ps_kv_pool_create(const ps_pool_desc* desc, ps_kv_pool** out);
+ps_status ps_kv_pool_destroy(ps_kv_pool* pool);
+
+/* Copies one chunk's cache entry into a slot, or out of it.
+ * k, v: device, [L, n_heads, head_dim] row-major in the compute dtype (k after
+ * RoPE).  chunk: the chunk id the ledger records for the slot (load only).
+ * Used to pre-fill a pool and by tests; not needed on the hot path. */
+ps_status ps_kv_pool_load(ps_kv_pool* pool, int32_t stream, int32_t block, int32_t step,
+                          int32_t slot, int32_t chunk, const void* k, const void* v,
+                          hipStream_t hs);
+ps_status ps_kv_pool_fetch(const ps_kv_pool* pool, int32_t stream, int32_t block,
+                           int32_t step, int32_t slot, void* k, void* v, hipStream_t hs);
+/* Copies the cached cross-attention keys/values of (stream, block) out:
+ * k, v device [n_ctx, n_heads, head_dim], compute dtype. */
+ps_status ps_context_fetch(const ps_kv_pool* pool, int32_t stream, int32_t block,
+                           void* k, void* v, hipStream_t hs);
+
+/* ----------------------------------------------------------------- block --
+ * One DiT block's weights, borrowed (device pointers, kept until
+ * ps_block_destroy).  Linear weights are [out, in] row-major in the compute
+ * dtype (y = x W^T + b).  With D = hidden, F = ffn:
+ *   wqkv [3D, D] rows (q | k | v)   wo [D, D]
+ *   wq2 [D, D]   wkv2 [2D, D] rows (k | v)   wo2 [D, D]
+ *   w1 [F, D]    w2 [D, F]
+ * Biases fp32: bqkv [3D], bo, bq2 [D], bkv2 [2D], bo2 [D], b1 [F], b2 [D].
+ * tmod: fp32 [6, D], the block's additive modulation table T_b; a task at
+ * timestep t uses m = e(t) + T_b with rows
+ * (shift1, scale1, gate1, shift2, scale2, gate2).
+ * block_index selects the block's region of the pool.
+ * Requirements: hidden % 64 == 0 and ffn % 64 == 0 (bf16), % 32 (fp32). */
+typedef struct {
+  int32_t hidden, n_heads, head_dim, ffn;
+  int32_t block_index;
+  ps_dtype dtype;
+  const void *wqkv, *wo, *wq2, *wkv2, *wo2, *w1, *w2;
+  const float *bqkv, *bo, *bq2, *bkv2, *bo2, *b1, *b2;
+  const float* tmod;
+} ps_block_desc;
+
+ps_status ps_block_create(const ps_block_desc* desc, ps_block** out);
+ps_status ps_block_destroy(ps_block* block);
+
+/* ------------------------------------------------------ timestep embedding --
+ * e(t) in R^{6 x D}, shared by all blocks:
+ *   phi(t) = [cos(1000 t w_j) | sin(1000 t w_j)], w_j = 10000^(-j/128), j < 128
+ *   u = SiLU(phi wt1^T + bt1) wt2^T + bt2;  e = SiLU(u) wp^T + bp.
+ * Weights fp32, borrowed: wt1 [D, 256], bt1 [D], wt2 [D, D], bt2 [D],
+ * wp [6D, D], bp [6D].  e(t) is computed once per distinct t (bitwise) and kept
+ * in a cache of `capacity` rows; the least recently used row is replaced when
+ * the cache is full. */
+typedef struct {
+  int32_t hidden;
+  int32_t capacity;
+  const float *wt1, *bt1, *wt2, *bt2, *wp, *bp;
+} ps_time_desc;
+
+ps_status ps_time_embed_create(const ps_time_desc* desc, ps_time_embed** out);
+ps_status ps_time_embed_destroy(ps_time_embed* te);
+/* Writes e(t) (fp32 [6, D], device) -- computes it if not cached. */
+ps_status ps_time_embed_get(ps_time_embed* te, float t, float* e, hipStream_t hs);
+
+/* --------------------------------------------------------------- context --
+ * Computes and caches the cross-attention keys/values of one stream's
+ * conditioning tokens for one block: k2 = ctx wkv2[:D]^T + bkv2[:D],
+ * v2 = ctx wkv2[D:]^T + bkv2[D:].  ctx: device [n_ctx, D], compute dtype.
+ * n_ctx: 8 .. max_ctx, a multiple of 8.  Must precede any ps_stage_batch
+ * whose tasks belong to that stream. */
+ps_status ps_context_set(ps_kv_pool* pool, const ps_block* block, int32_t stream,
+                         const void* ctx, int32_t n_ctx, hipStream_t hs);
+
+/* ----------------------------------------------------------------- stage --
+ * One stage task (host struct).  The task runs `block` at `step` for chunk
+ * `chunk` of `stream`, with modulation e(timestep) + T_b.  Its keys/values go
+ * to slot write_slot of (stream, block, step); its self-attention reads the
+ * slots read_slots[0 .. n_read-1] (chronological, oldest first) followed by
+ * its own write_slot. */
+typedef struct {
+  int32_t stream, chunk, step;
+  float timestep;
+  int32_t write_slot;
+  int32_t n_read;
+  int32_t read_slots[PS_MAX_WINDOW];
+} ps_task;
+
+/* Runs one block on a batch of stage tasks (tasks may mix chunks, steps and
+ * streams):
+ *   y  = LN(h)(1 + scale1) + shift1;  q, k, v = y Wqkv^T + bqkv;
+ *   RoPE3D(q, k); (k, v) -> slot write_slot;
+ *   h += gate1 * (SelfAttn(q, window keys/values) wo^T + bo)
+ *   h += CrossAttn(LN(h) wq2^T + bq2, cached ctx keys/values) wo2^T + bo2
+ *   h += gate2 * (GELU_tanh((LN(h)(1 + scale2) + shift2) w1^T + b1) w2^T + b2)
+ * LN is per row without affine, eps 1e-6; attention scale 1/sqrt(head_dim).
+ * All keys/values of the batch are written before any task reads (so a task
+ * may read the slot another task of the same batch writes).
+ * tasks: host [n_tasks].  h_in, h_out: device fp32 [n_tasks * L, D], task i
+ * owning rows i*L .. i*L+L-1; h_in == h_out is allowed.  Two tasks may not
+ * write the same slot, and a write slot may not be read by the same task.
+ * Errors: PS_ERR_INVALID_ARG, PS_ERR_SLOT_CONFLICT (ledger on), PS_ERR_HIP,
+ * PS_ERR_OUT_OF_MEMORY (workspace growth). */
+ps_status ps_stage_batch(ps_kv_pool* pool, const ps_block* block, ps_time_embed* te,
+                         const ps_task* tasks, int32_t n_tasks, const float* h_in,
+                         float* h_out, hipStream_t hs);
+
+/* ----------------------------------------------------------------- euler --
+ * Flow-matching Euler step after the last block: for task i,
+ *   x[i] <- x[i] - dt[i] * v[i],  dt[i] = t_s - t_{s+1} (t_S = 0).
+ * x: device fp32 [n_tasks * tokens, hidden]; v: device [n_tasks * tokens,
+ * hidden] of v_dtype (PS_F32 or PS_BF16); dt: host fp32 [n_tasks]. */
+ps_status ps_euler_update(float* x, const void* v, const float* dt, int32_t n_tasks,
+                          int32_t tokens, int32_t hidden, ps_dtype v_dtype,
+                          hipStream_t hs);
+
+/* Message of the last failure on this host thread ("" if none). */
+const char* ps_last_error(void);
+
+/* ----------------------------------------------------------------- trace --
+ * Per-kernel timing of the stage path.  While tracing is on, every kernel
+ * that ps_stage_batch and ps_euler_update launch is bracketed by HIP events
+ * recorded on the caller's stream; ps_trace_collect() waits for the pending
+ * events and adds each kernel's duration to its named entry.  Names:
+ * "put_tasks", "modulation", "ln1", "qkv", "attn_self", "o_proj", "ln2",
+ * "xq_proj", "attn_cross", "xo_proj", "ln3", "ffn1", "ffn2", "euler".
+ * ps_trace_enable(1) clears the statistics; tracing adds an event pair per
+ * kernel, so it is off by default. */
+ps_status ps_trace_enable(int32_t on);
+ps_status ps_trace_collect(void);
+int32_t ps_trace_count(void);
+/* Entry i (0 .. count-1): name (static string), launches, total milliseconds. */
+ps_status ps_trace_entry(int32_t i, const char** name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PS_H_ */

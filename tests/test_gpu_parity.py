@@ -1,0 +1,271 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Bar: max |err| / RMS(ref) <= 3e-2 with bf16 operands and <= 1e-4 with fp32
+operands, on every tensor compared (stage output, its branch delta and the
+cache entries written)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from autoregressive_denoising_dit_amd import runtime
+from autoregressive_denoising_dit_amd._lib import PsError, PS_ERR_SLOT_CONFLICT, PS_ERR_INVALID_ARG
+from synthetic import C1, C2, C3, C4, C5, inputs, with_
+from tests.gpu_util import (StageCase, host, make_block, make_pool, make_te, rel_err, say, to_dev, tol)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_case(case, task_ids=None, rows=None):
+    cfg, L = case.cfg, case.cfg.tokens
+    t = tol(cfg)
+    ids = list(range(len(case.tasks))) if task_ids is None else task_ids
+    for i in ids:
+        got = case.gpu_h_out[i * L:(i + 1) * L]
+        h = case.h_in[i * L:(i + 1) * L]
+        if rows is not None:
+            got, h = got[rows], h[rows]
+        ref = case.ref_h_out[i]
+        e_out = rel_err(got, ref)
+        e_delta = rel_err(got - h, ref - h)
+        say(f"task {i} {case.tasks[i]}: h_out err {e_out:.2e}, branch delta err {e_delta:.2e}")
+        assert e_out <= t, (i, e_out)
+        assert e_delta <= t, (i, e_delta)
+        key = (case.tasks[i][0], case.tasks[i][1], case.tasks[i][2])
+        if key in case.ref_kv:
+            k_ref, v_ref = case.ref_kv[key]
+            k_got, v_got = case.gpu_kv[key]
+            ek, ev = rel_err(k_got, k_ref), rel_err(v_got, v_ref)
+            say(f"task {i}: cache k err {ek:.2e}, v err {ev:.2e}")
+            assert ek <= t and ev <= t
+
+
+# ----------------------------------------------------------------- pieces
+@pytest.mark.parametrize("cfg", [C1, C2], ids=["fp32_d128", "w1536"])
+def test_time_embedding(cfg):
+    tw = inputs.time_weights(cfg, 0)
+    te = make_te(cfg, tw, capacity=2)
+    for t in (1.0, 0.75, 0.3, 1.0, 0.0):   # more distinct t than capacity: eviction path
+        say("time embed", cfg.name, t)
+        got = host(te.get(t))
+        ref = oracle.time_embedding(t, tw)
+        assert rel_err(got, ref) <= 1e-4
+
+
+@pytest.mark.parametrize("cfg", [C1, C2], ids=["fp32", "bf16"])
+def test_context_keys_values(cfg):
+    w = inputs.block_weights(cfg, 0, 0)
+    pool = make_pool(cfg, n_streams=2, n_blocks=1)
+    blk = make_block(cfg, w)
+    td = runtime.TORCH_DTYPE[runtime.ps_dtype(cfg.dtype)]
+    for sg in (1, 0):
+        ctx = inputs.context(cfg, sg, 0)
+        say("context", cfg.name, sg)
+        pool.context_set(blk, sg, to_dev(ctx, td))
+        k, v = pool.context_fetch(sg, 0, cfg.n_ctx)
+        rk, rv = oracle.context_kv(ctx, w, cfg.heads)
+        assert rel_err(host(k), rk) <= tol(cfg) / 3
+        assert rel_err(host(v), rv) <= tol(cfg) / 3
+
+
+@pytest.mark.parametrize("vdt", [torch.float32, torch.bfloat16])
+def test_euler_update(vdt):
+    L, D, n = 64, 128, 3
+    r = np.random.default_rng(3)
+    x = r.standard_normal((n * L, D)).astype(np.float32)
+    v = r.standard_normal((n * L, D)).astype(np.float32)
+    dt = [0.5, 0.25, 0.125]
+    xd, vd = to_dev(x, torch.float32), to_dev(v, vdt)
+    say("euler", vdt)
+    runtime.euler_update(xd, vd, dt, L, D)
+    vv = host(vd)
+    ref = x.astype(np.float64) - np.repeat(np.array(dt), L)[:, None] * vv
+    assert rel_err(host(xd), ref) <= 1e-6
+
+
+def test_pool_load_fetch_roundtrip():
+    cfg = C1
+    pool = make_pool(cfg, n_streams=1, n_blocks=1)
+    k, v = inputs.cache_entry(cfg, 0, 0, 1, 5, 0)
+    say("pool roundtrip")
+    pool.load(0, 0, 1, 2, 5, to_dev(k, torch.float32), to_dev(v, torch.float32))
+    k2, v2 = pool.fetch(0, 0, 1, 2)
+    assert np.array_equal(host(k2), k) and np.array_equal(host(v2), v)
+
+
+# ------------------------------------------------------------ stage batches
+def test_stage_fp32_tiny_mixed_batch():
+    """C1 shapes, fp32: tasks of different chunks, steps and window fill."""
+    cfg = C1
+    tasks = [(0, 0, 0, 0), (0, 3, 1, 2), (0, 2, 0, 2), (0, 1, 1, 1)]
+    case = StageCase(cfg, tasks).run_gpu()
+    case.run_oracle()
+    _check_case(case)
+
+
+def test_stage_fp32_reads_same_batch_write():
+    """Two chunks of one step in one batch (k = 2): chunk c + 1 reads what chunk c
+    writes in the same call."""
+    cfg = C1
+    tasks = [(0, 4, 1, 2), (0, 5, 1, 2), (0, 2, 0, 2), (0, 3, 0, 2)]
+    case = StageCase(cfg, tasks, n_slots=cfg.window + 2).run_gpu(h_out_same=True)
+    case.run_oracle()
+    _check_case(case)
+
+
+def test_stage_bf16_tiny_shapes():
+    cfg = with_(C1, dtype="bf16")
+    tasks = [(0, 3, 1, 2), (1, 2, 0, 2), (0, 0, 1, 0)]
+    case = StageCase(cfg, tasks).run_gpu()
+    case.run_oracle()
+    _check_case(case)
+
+
+def test_stage_c2_single_task_full():
+    """Wan2.1-1.3B-shaped stage at batch 1, full window, every output row."""
+    cfg = C2
+    case = StageCase(cfg, [(0, 7, 2, 3)]).run_gpu()
+    case.run_oracle()
+    _check_case(case)
+
+
+def test_stage_c3_mixed_steps_sampled():
+    """1.3B shape, a time-shared batch of 8 tasks: 2 chunks per step at all 4
+    steps (k = 2, ring W + 2); sampled rows of two tasks checked."""
+    cfg = C3
+    tasks = []
+    for s in range(4):
+        for j in range(2):
+            c = 2 * (5 - s) + j
+            tasks.append((0, c, s, min(cfg.window, c)))
+    case = StageCase(cfg, tasks, n_slots=cfg.window + 2).run_gpu()
+    rows = np.array([0, 1, 100, 777, 1200, 1559])
+    case.run_oracle(task_ids=[1, 6], rows=rows)
+    _check_case(case, task_ids=[1, 6], rows=rows)
+
+
+def test_stage_c4_sampled():
+    cfg = C4
+    tasks = [(0, 9, 3, 3), (0, 12, 0, 3)]
+    case = StageCase(cfg, tasks).run_gpu()
+    rows = np.array([0, 43, 44, 901, 1759])
+    case.run_oracle(task_ids=[0, 1], rows=rows)
+    _check_case(case, task_ids=[0, 1], rows=rows)
+
+
+def test_stage_c5_sixteen_streams_sampled():
+    """14B-shaped stage, the batch of 16 tasks from 16 streams at mixed steps
+    that the benchmark times; sampled rows of two tasks checked."""
+    cfg = C5
+    tasks = [(i, 10 + i // 4, (i * 3) % 4, 3) for i in range(16)]
+    case = StageCase(cfg, tasks, share_prefill=True).run_gpu()
+    rows = np.array([0, 517, 1559])
+    case.run_oracle(task_ids=[0, 13], rows=rows)
+    _check_case(case, task_ids=[0, 13], rows=rows)
+
+
+# ------------------------------------------------------------- schedules
+def _schedule_inputs(cfg, n_chunks, n_streams, seed=0):
+    blocks = [inputs.block_weights(cfg, b, seed) for b in range(cfg.n_blocks)]
+    tw = inputs.time_weights(cfg, seed)
+    ctxs = [inputs.context(cfg, sg, seed) for sg in range(n_streams)]
+    lat = {(sg, c): inputs.latent(cfg, sg, c, seed) for sg in range(n_streams) for c in range(n_chunks)}
+    return blocks, tw, ctxs, lat
+
+
+def _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, n_streams, k):
+    from autoregressive_denoising_dit_amd.schedule import StaggeredRunner
+    td = runtime.TORCH_DTYPE[runtime.ps_dtype(cfg.dtype)]
+    pool = make_pool(cfg, n_streams=n_streams, n_blocks=cfg.n_blocks, n_slots=cfg.window + k)
+    blks = [make_block(cfg, w, b) for b, w in enumerate(blocks)]
+    te = make_te(cfg, tw)
+    for b, blk in enumerate(blks):
+        for sg in range(n_streams):
+            pool.context_set(blk, sg, to_dev(ctxs[sg], td))
+    x = torch.stack([torch.stack([to_dev(lat[(sg, c)], torch.float32) for sg in range(n_streams)])
+                     for c in range(n_chunks)]).contiguous()
+    run = StaggeredRunner(pool, blks, te, cfg.timesteps, cfg.window, k, n_streams)
+    run.run(x, n_chunks)
+    torch.cuda.synchronize()
+    return host(x)
+
+
+@pytest.mark.parametrize("k,n_streams", [(1, 1), (2, 1), (1, 2)])
+def test_schedule_c1_matches_oracle(k, n_streams):
+    """The tiny configuration end to end (2 blocks x 2 steps, 4 chunks of 64
+    tokens, window 2, fp32): staggered on the GPU vs sequential in the oracle."""
+    cfg, n_chunks = C1, 4
+    blocks, tw, ctxs, lat = _schedule_inputs(cfg, n_chunks, n_streams)
+    say("schedule c1", k, n_streams)
+    gx = _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, n_streams, k)
+    ox, _ = oracle.run_schedule(cfg, blocks, tw, lambda sg, c: lat[(sg, c)], ctxs, n_chunks,
+                                order="sequential")
+    for c in range(n_chunks):
+        for sg in range(n_streams):
+            e = rel_err(gx[c, sg], ox[(sg, c)])
+            say(f"chunk {c} stream {sg}: x^S err {e:.2e}")
+            assert e <= 1e-4
+
+
+def test_schedule_batch_invariance_bitwise_c3_shape():
+    """A task's result does not depend on its batch companions: the staggered
+    run (batches of 8 mixed-step tasks) and k = 1 run at 1.3B width give
+    bitwise equal latents (2 blocks, 5 chunks)."""
+    cfg = with_(C3, n_blocks=2)
+    n_chunks = 5
+    blocks, tw, ctxs, lat = _schedule_inputs(cfg, n_chunks, 1)
+    say("batch invariance c3 shape")
+    a = _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, 1, 2)
+    b = _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, 1, 1)
+    assert np.array_equal(a, b)
+    assert np.all(np.isfinite(a))
+
+
+# ------------------------------------------------------------ error paths
+def test_slot_ledger_rejects_stale_read():
+    cfg = C1
+    pool = make_pool(cfg, n_streams=1, n_blocks=1, check_slots=True)
+    blk = make_block(cfg, inputs.block_weights(cfg, 0, 0))
+    te = make_te(cfg, inputs.time_weights(cfg, 0))
+    pool.context_set(blk, 0, to_dev(inputs.context(cfg, 0, 0), torch.float32))
+    k, v = inputs.cache_entry(cfg, 0, 0, 0, 1, 0)
+    pool.load(0, 0, 0, 1, 1, to_dev(k, torch.float32), to_dev(v, torch.float32))
+    h = torch.zeros((cfg.tokens, cfg.hidden), dtype=torch.float32, device="cuda")
+    # chunk 3 expects chunks 1, 2 in its read slots; slot 2 holds nothing
+    bad = runtime.make_task(0, 3, 0, 1.0, 0, [1, 2])
+    with pytest.raises(PsError) as ei:
+        runtime.stage_batch(pool, blk, te, [bad], h, h)
+    assert ei.value.status == PS_ERR_SLOT_CONFLICT
+    # two tasks writing one slot
+    t1 = runtime.make_task(0, 2, 0, 1.0, 0, [1])
+    t2 = runtime.make_task(0, 2, 0, 1.0, 0, [1])
+    h2 = torch.zeros((2 * cfg.tokens, cfg.hidden), dtype=torch.float32, device="cuda")
+    with pytest.raises(PsError) as ei:
+        runtime.stage_batch(pool, blk, te, [t1, t2], h2, h2)
+    assert ei.value.status == PS_ERR_SLOT_CONFLICT
+    # a valid call still works after the rejections
+    ok = runtime.make_task(0, 2, 0, 1.0, 2, [1])
+    runtime.stage_batch(pool, blk, te, [ok], h, h)
+    torch.cuda.synchronize()
+    assert torch.isfinite(h).all()
+
+
+def test_invalid_arguments_rejected():
+    cfg = C1
+    pool = make_pool(cfg, n_streams=1, n_blocks=1)
+    blk = make_block(cfg, inputs.block_weights(cfg, 0, 0))
+    te = make_te(cfg, inputs.time_weights(cfg, 0))
+    h = torch.zeros((cfg.tokens, cfg.hidden), dtype=torch.float32, device="cuda")
+    # context not set yet
+    with pytest.raises(PsError) as ei:
+        runtime.stage_batch(pool, blk, te, [runtime.make_task(0, 0, 0, 1.0, 0, [])], h, h)
+    assert ei.value.status == PS_ERR_INVALID_ARG
+    pool.context_set(blk, 0, to_dev(inputs.context(cfg, 0, 0), torch.float32))
+    for bad in (runtime.make_task(1, 0, 0, 1.0, 0, []),       # stream out of range
+                runtime.make_task(0, 0, 2, 1.0, 0, []),       # step out of range
+                runtime.make_task(0, 0, 0, 1.0, 9, []),       # slot out of range
+                runtime.make_task(0, 1, 0, 1.0, 0, [0]),      # reads its own write slot
+                runtime.make_task(0, 0, 0, float("nan"), 0, [])):
+        with pytest.raises(PsError) as ei:
+            runtime.stage_batch(pool, blk, te, [bad], h, h)
+        assert ei.value.status == PS_ERR_INVALID_ARG
