@@ -191,8 +191,8 @@ __global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restr
         pf = __builtin_bit_cast(u32x4, pb);
       } else {
         const int t = u >> 2, r0 = (u & 3) * 4;
-        pf = u32x4{__builtin_bit_cast(uint32_t, s[t][r0]), __builtin_bit_cast(uint32_t, s[t][r0 + 1]),
-                   __builtin_bit_cast(uint32_t, s[t][r0 + 2]), __builtin_bit_cast(uint32_t, s[t][r0 + 3])};
+        const f32x4 p4 = {s[t][r0], s[t][r0 + 1], s[t][r0 + 2], s[t][r0 + 3]};
+        pf = __builtin_bit_cast(u32x4, p4);
       }
 #pragma unroll
       for (int i = 0; i < HD / 32; ++i) {

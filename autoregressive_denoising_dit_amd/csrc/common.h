@@ -41,14 +41,14 @@ template <>
 struct Mfma<float> {
   static constexpr int kPerUnit = 8;
   __device__ __forceinline__ static void unit(f32x16& acc, u32x4 a, u32x4 b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.x),
-                                               __builtin_bit_cast(float, b.x), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.y),
-                                               __builtin_bit_cast(float, b.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.z),
-                                               __builtin_bit_cast(float, b.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.w),
-                                               __builtin_bit_cast(float, b.w), acc, 0, 0, 0);
+    // bit-cast whole vectors: a bit-cast of a single vector element would read
+    // the vector's first element
+    const f32x4 fa = __builtin_bit_cast(f32x4, a);
+    const f32x4 fb = __builtin_bit_cast(f32x4, b);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[0], fb[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[1], fb[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[2], fb[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[3], fb[3], acc, 0, 0, 0);
   }
 };
 
