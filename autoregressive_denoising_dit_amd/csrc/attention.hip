@@ -32,10 +32,31 @@ namespace ps {
 namespace {
 
 constexpr int NT = 256, QT = 128, KT = 64;
+// Lazy rescaling: the running max m used in exp2(s - m) is raised only when a
+// tile's logits exceed it by more than this (log2 units), so probabilities stay
+// <= 2^8 and the O / l rescale is skipped on most tiles.  O / l is unchanged.
+constexpr float kLazy = 8.0f;
+
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int full = (total / 8) * 8;
+  if (id >= full) return id;
+  return (id % 8) * (total / 8) + id / 8;
+}
+
+// bf16: LDS row r of a key tile holds key perm16(r): within each group of 16
+// rows the middle two quads are swapped, so that the S^T accumulator rows a
+// half-wave holds ({4g..4g+3, 8+4g..8+4g+3}) are keys 8g..8g+7 -- exactly the
+// 8 contiguous keys of its V^T operand chunk in the P V product.
+__device__ __forceinline__ int perm16(int r) {
+  const int q = (r >> 2) & 3;
+  const int qs = (q == 1) ? 2 : (q == 2) ? 1 : q;
+  return (r & ~15) | (qs << 2) | (r & 3);
+}
 
 template <typename T, int HD>
-__global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restrict__ out,
-                                             PoolGeo pg, const DevTask* __restrict__ tasks, int cross) {
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+k_attn(const T* __restrict__ q, T* __restrict__ out, PoolGeo pg, const DevTask* __restrict__ tasks, int cross,
+       int n_qt, int n_tasks) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KCH = HD / VEC;     // 16-byte chunks per K row
   constexpr int VCH = KT / VEC;     // 16-byte chunks per V^T row
@@ -49,11 +70,15 @@ __global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restr
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int h = blockIdx.y, task = blockIdx.z;
+  const int total = n_qt * pg.H * n_tasks;
+  const int pid = xcd_remap(blockIdx.x, total);   // a (task, head)'s query tiles share an XCD
+  const int qt = pid % n_qt;
+  const int h = (pid / n_qt) % pg.H;
+  const int task = pid / (n_qt * pg.H);
   const DevTask& tk = tasks[task];
   const int L = pg.L, D = pg.H * HD;
 
-  // key segments
+  // key segments: self = read slots then the write slot; cross = the context
   int n_seg, seg_valid, seg_stride;
   if (cross) {
     n_seg = 1; seg_valid = tk.ctx_len; seg_stride = pg.max_ctx;
@@ -61,41 +86,54 @@ __global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restr
     n_seg = tk.n_seg; seg_valid = L; seg_stride = L;
   }
   const int n_keys = n_seg * seg_valid;
-  auto seg_base = [&](int sgi) -> const T* {
-    if (cross) return static_cast<const T*>(pg.ctx) + (size_t)tk.ctx_region * pg.ctx_elems;
-    return static_cast<const T*>(pg.kv) +
-           ((size_t)tk.region * pg.n_slots + tk.slots[sgi]) * pg.slot_elems;
+  const T* seg_ptr[PS_MAX_WINDOW + 1];
+  if (cross) {
+    seg_ptr[0] = static_cast<const T*>(pg.ctx) + (size_t)tk.ctx_region * pg.ctx_elems;
+  } else {
+#pragma unroll
+    for (int i = 0; i < PS_MAX_WINDOW + 1; ++i)
+      seg_ptr[i] = static_cast<const T*>(pg.kv) +
+                   ((size_t)tk.region * pg.n_slots + tk.slots[i < n_seg ? i : 0]) * pg.slot_elems;
+  }
+  auto locate = [&](int j, int& sgi, int& tok) {
+    if (cross) {
+      sgi = 0; tok = j;
+    } else {
+      sgi = (int)pg.div_L.div((uint32_t)j);
+      tok = j - sgi * L;
+    }
   };
-  const size_t v_off = (size_t)pg.H * seg_stride * HD;
+  const size_t k_off = (size_t)h * seg_stride * HD;
+  const size_t v_off = (size_t)pg.H * seg_stride * HD + (size_t)h * HD * seg_stride;
 
   // this lane's query and its Q fragments (B operand of S^T = K Q^T)
-  const int qi = blockIdx.x * QT + wave * 32 + l32;
+  const int qi = qt * QT + wave * 32 + l32;
   const int qc = min(qi, L - 1);
   const T* qrow = q + ((size_t)task * L + qc) * D + (size_t)h * HD;
   u32x4 qf[NU_QK];
 #pragma unroll
   for (int u = 0; u < NU_QK; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + (2 * u + g) * VEC);
 
-  // per-thread load slots
   u32x4 kr[KLD], vr[VLD];
   auto fetch = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
       const int e = tid + NT * i;
       const int row = e / KCH, c = e % KCH;
-      const int j = min(tile * KT + row, n_keys - 1);
-      const int sgi = j / seg_valid, tok = j - sgi * seg_valid;
-      kr[i] = *reinterpret_cast<const u32x4*>(seg_base(sgi) + ((size_t)h * seg_stride + tok) * HD +
-                                              c * VEC);
+      const int key = kBf16 ? perm16(row) : row;
+      const int j = min(tile * KT + key, n_keys - 1);
+      int sgi, tok;
+      locate(j, sgi, tok);
+      kr[i] = *reinterpret_cast<const u32x4*>(seg_ptr[sgi] + k_off + (size_t)tok * HD + c * VEC);
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int e = tid + NT * i;
       const int f = e / VCH, c = e % VCH;
       const int j0 = min(tile * KT + c * VEC, n_keys - VEC);
-      const int sgi = j0 / seg_valid, tok = j0 - sgi * seg_valid;
-      vr[i] = *reinterpret_cast<const u32x4*>(seg_base(sgi) + v_off +
-                                              ((size_t)h * HD + f) * seg_stride + tok);
+      int sgi, tok;
+      locate(j0, sgi, tok);
+      vr[i] = *reinterpret_cast<const u32x4*>(seg_ptr[sgi] + v_off + (size_t)f * seg_stride + tok);
     }
   };
   auto stash = [&](int buf) {
@@ -109,18 +147,7 @@ __global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restr
     for (int i = 0; i < VLD; ++i) {
       const int e = tid + NT * i;
       const int f = e / VCH, c = e % VCH;
-      if constexpr (kBf16) {
-        // keys of a 16-key group are kept in the order {0-3, 8-11, 4-7, 12-15}
-        // so that half-wave g reads its 8 keys {4g..4g+3, 8+4g..8+4g+3} as one
-        // 16-byte chunk, matching the probabilities it holds.
-        const int grp = c >> 1, half = c & 1;
-        u32x2* lo = reinterpret_cast<u32x2*>(&vs[buf][f * VCH + ((2 * grp) ^ (f & 7))]);
-        u32x2* hi = reinterpret_cast<u32x2*>(&vs[buf][f * VCH + ((2 * grp + 1) ^ (f & 7))]);
-        lo[half] = u32x2{vr[i].x, vr[i].y};
-        hi[half] = u32x2{vr[i].z, vr[i].w};
-      } else {
-        vs[buf][f * VCH + (c ^ (f & 7))] = vr[i];
-      }
+      vs[buf][f * VCH + (c ^ (f & 7))] = vr[i];
     }
   };
 
@@ -129,7 +156,10 @@ __global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restr
   for (int i = 0; i < HD / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = 0.0f, l_run = 0.0f;
+  f32x16 negm;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negm[r] = 0.0f;
 
   const int n_tiles = (n_keys + KT - 1) / KT;
   fetch(0);
@@ -139,45 +169,54 @@ __global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restr
     const int buf = tile & 1;
     if (tile + 1 < n_tiles) fetch(tile + 1);
 
-    // S^T for the 64 keys of this tile: two 32-key row tiles
+    // S^T - m for the 64 keys of this tile (the accumulators start at -m)
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = 0.0f;
+      s[t] = negm;
 #pragma unroll
       for (int u = 0; u < NU_QK; ++u) {
         const u32x4 kf = ks[buf][(t * 32 + l32) * KCH + ((2 * u + g) ^ (l32 & 7))];
         Mfma<T>::unit(s[t], kf, qf[u]);
       }
     }
-    // mask keys past the end, then the online softmax update
-    float mloc = -INFINITY;
+    if ((tile + 1) * KT > n_keys) {   // ragged last tile
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = t * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
+          const int key = tile * KT + (kBf16 ? perm16(row) : row);
+          if (key >= n_keys) s[t][r] = -INFINITY;
+        }
+    }
+    float mt = s[0][0];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = tile * KT + t * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-        if (key >= n_keys) s[t][r] = -INFINITY;
-        mloc = fmaxf(mloc, s[t][r]);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[t][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool need = (tile == 0) || (mt > kLazy);
+    if (__any(need)) {
+      const float shift = need ? mt : 0.0f;
+      const float alpha = exp2f(-shift);
+      m_run += shift;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[r] = -m_run;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[t][r] -= shift;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < HD / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[t][r] = exp2f(s[t][r] - m_new);
-        psum += s[t][r];
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < HD / 32; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      for (int r = 0; r < 16; ++r) s[t][r] = exp2f(s[t][r]);
 
     // O^T += V^T P^T
 #pragma unroll
@@ -189,9 +228,18 @@ __global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restr
 #pragma unroll
         for (int r = 0; r < 8; ++r) pb[r] = (bf16)s[t][r0 + r];
         pf = __builtin_bit_cast(u32x4, pb);
+        // row sum of the probabilities as the MFMA sees them (bf16)
+        typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bf16x2 pr = {pb[2 * r], pb[2 * r + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l_run, false);
+        }
       } else {
         const int t = u >> 2, r0 = (u & 3) * 4;
         const f32x4 p4 = {s[t][r0], s[t][r0 + 1], s[t][r0 + 2], s[t][r0 + 3]};
+        l_run += (p4[0] + p4[1]) + (p4[2] + p4[3]);
         pf = __builtin_bit_cast(u32x4, p4);
       }
 #pragma unroll
@@ -235,11 +283,12 @@ __global__ void __launch_bounds__(NT) k_attn(const T* __restrict__ q, T* __restr
 template <typename T>
 hipError_t launch_attention(bool cross, const T* q, T* out, const PoolGeo& pg, const DevTask* tt,
                             int n_tasks, hipStream_t s) {
-  dim3 grid((pg.L + QT - 1) / QT, pg.H, n_tasks), block(NT);
+  const int n_qt = (pg.L + QT - 1) / QT;
+  dim3 grid(n_qt * pg.H * n_tasks), block(NT);
   if (pg.d == 128) {
-    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, q, out, pg, tt, cross ? 1 : 0);
+    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, q, out, pg, tt, cross ? 1 : 0, n_qt, n_tasks);
   } else if (pg.d == 64) {
-    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, q, out, pg, tt, cross ? 1 : 0);
+    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, q, out, pg, tt, cross ? 1 : 0, n_qt, n_tasks);
   } else {
     return hipErrorInvalidValue;
   }
