@@ -18,6 +18,8 @@
 // ids land on the same XCD (the dispatcher deals workgroups to the 8 XCDs
 // round-robin, each XCD has its own L2), then walked in groups of 8 tile rows
 // so that the tiles an XCD runs together share operand panels in its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -25,10 +27,12 @@ namespace ps {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, ROWB = 128, NT = 256;
-constexpr int CPR = ROWB / 16;  // 16-byte chunks per LDS row (8)
+constexpr int BM = 256, BN = 256, ROWB = 64, NT = 256;
+constexpr int CPR = ROWB / 16;  // 16-byte chunks per LDS row (4)
+constexpr int NSTAGE = 4;       // LDS ring of operand stages
 constexpr int EPITCH = 65;      // fp32 row pitch of the epilogue staging (64 columns + 1)
-constexpr int OPER_BYTES = 2 * (BM + BN) * ROWB;        // double-buffered operand tiles
+constexpr int STAGE_CH = (BM + BN) * CPR;               // 16-byte chunks per stage
+constexpr int OPER_BYTES = NSTAGE * STAGE_CH * 16;      // 4 x 32 KB
 constexpr int STAGE_BYTES = 4 * 128 * EPITCH * 4;      // 4 waves x 128 rows x pitch
 constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
 
@@ -44,6 +48,10 @@ __device__ __forceinline__ float gelu_tanh(float z) {
 }
 
 // Epilogue of one wave's 128 x 64 staged block (rows rbase.., columns cbase..).
+// Rows (or columns) are processed EB at a time so that EB independent global
+// loads and stores are in flight per lane instead of one.
+constexpr int EB = 8;
+
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue_half(const float* stg, int rbase, int cbase, int lane, int M, int N,
                                               const EpiArgs& ep, const DevTask* __restrict__ tasks) {
@@ -51,6 +59,7 @@ __device__ __forceinline__ void epilogue_half(const float* stg, int rbase, int c
   const bool col_ok = col < N;
   if (cbase >= N) return;
   const int nrows = min(128, M - rbase);
+  if (nrows <= 0) return;
   const PoolGeo& pg = ep.pool;
   if constexpr (EPI == EPI_QKV || EPI == EPI_CTX_KV) {
     const int D = pg.H * pg.d;
@@ -77,13 +86,17 @@ __device__ __forceinline__ void epilogue_half(const float* stg, int rbase, int c
           tok = row;
           vt = static_cast<T*>(ep.ctx_base) + (size_t)pg.H * pg.max_ctx * pg.d;
         }
-        for (int c2 = 0; c2 < 64; ++c2) {
-          const int cg = cbase + c2;
-          if (cg >= N) break;
-          const float val = stg[rr * EPITCH + c2] + ep.bias[cg];
-          const int cc = cg - part * D;
-          const int hh = cc >> ep.d_shift, dd = cc & (pg.d - 1);
-          if (row_ok) vt[((size_t)hh * pg.d + dd) * stride + tok] = from_f32<T>(val);
+        const int ncol = min(64, N - cbase);
+        for (int c0 = 0; c0 < ncol; c0 += EB) {
+          float val[EB];
+#pragma unroll
+          for (int k = 0; k < EB; ++k) val[k] = stg[rr * EPITCH + c0 + k] + ep.bias[min(cbase + c0 + k, N - 1)];
+#pragma unroll
+          for (int k = 0; k < EB; ++k) {
+            const int cc = cbase + c0 + k - part * D;
+            const int hh = cc >> ep.d_shift, dd = cc & (pg.d - 1);
+            if (row_ok && c0 + k < ncol) vt[((size_t)hh * pg.d + dd) * stride + tok] = from_f32<T>(val[k]);
+          }
         }
       }
       return;
@@ -110,55 +123,84 @@ __device__ __forceinline__ void epilogue_half(const float* stg, int rbase, int c
       } else {
         seg = 2; pi = (dd - pg.seg_f - pg.seg_h) >> 1;
       }
-      for (int rr = 0; rr < nrows; ++rr) {
-        const int row = rbase + rr;
-        const int ti = (int)pg.div_L.div(row);
-        const int tok = row - ti * pg.L;
-        const int yx = (int)pg.div_cols.div(tok);
-        float2 cs;
-        if (seg == 0) {
-          const int fl = (int)pg.div_plane.div(tok);
-          cs = ep.rope_f[(ti * pg.frames + fl) * (pg.seg_f / 2) + pi];
-        } else if (seg == 1) {
-          const int yy = yx - (int)pg.div_rows.div(yx) * pg.rows;
-          cs = pg.rope_y[yy * (pg.seg_h / 2) + pi];
-        } else {
-          const int xx = tok - yx * pg.cols;
-          cs = pg.rope_x[xx * (pg.seg_w / 2) + pi];
+      for (int r0 = 0; r0 < nrows; r0 += EB) {
+        float2 cs[EB];
+        int tis[EB], toks[EB];
+#pragma unroll
+        for (int k = 0; k < EB; ++k) {
+          const int row = rbase + min(r0 + k, nrows - 1);
+          const int ti = (int)pg.div_L.div(row);
+          const int tok = row - ti * pg.L;
+          const int yx = (int)pg.div_cols.div(tok);
+          tis[k] = ti;
+          toks[k] = tok;
+          if (seg == 0) {
+            const int fl = (int)pg.div_plane.div(tok);
+            cs[k] = ep.rope_f[(ti * pg.frames + fl) * (pg.seg_f / 2) + pi];
+          } else if (seg == 1) {
+            const int yy = yx - (int)pg.div_rows.div(yx) * pg.rows;
+            cs[k] = pg.rope_y[yy * (pg.seg_h / 2) + pi];
+          } else {
+            const int xx = tok - yx * pg.cols;
+            cs[k] = pg.rope_x[xx * (pg.seg_w / 2) + pi];
+          }
         }
-        const float val = stg[rr * EPITCH + lane] + bias;
-        const float partner = stg[rr * EPITCH + (lane ^ 1)] + bias_p;
-        const float out = val * cs.x + sgn * partner * cs.y;
-        if (!col_ok) continue;
-        if (part == 0) {
-          static_cast<T*>(ep.out)[(size_t)row * D + cc] = from_f32<T>(out * ep.out_scale);
-        } else {
-          const DevTask& tk = tasks[ti];
-          T* kb = static_cast<T*>(pg.kv) +
-                  ((size_t)tk.region * pg.n_slots + tk.slots[tk.n_seg - 1]) * pg.slot_elems;
-          kb[((size_t)hh * pg.L + tok) * pg.d + dd] = from_f32<T>(out);
+#pragma unroll
+        for (int k = 0; k < EB; ++k) {
+          const int rr = r0 + k;
+          if (rr >= nrows || !col_ok) continue;
+          const int row = rbase + rr;
+          const float val = stg[rr * EPITCH + lane] + bias;
+          const float partner = stg[rr * EPITCH + (lane ^ 1)] + bias_p;
+          const float o = val * cs[k].x + sgn * partner * cs[k].y;
+          if (part == 0) {
+            static_cast<T*>(ep.out)[(size_t)row * D + cc] = from_f32<T>(o * ep.out_scale);
+          } else {
+            const DevTask& tk = tasks[tis[k]];
+            T* kb = static_cast<T*>(pg.kv) +
+                    ((size_t)tk.region * pg.n_slots + tk.slots[tk.n_seg - 1]) * pg.slot_elems;
+            kb[((size_t)hh * pg.L + toks[k]) * pg.d + dd] = from_f32<T>(o);
+          }
         }
       }
       return;
     }
   } else {
     const float bias = col_ok ? ep.bias[col] : 0.0f;
-    for (int rr = 0; rr < nrows; ++rr) {
-      const int row = rbase + rr;
-      const float val = stg[rr * EPITCH + lane] + bias;
-      if (!col_ok) continue;
-      const size_t o = (size_t)row * N + col;
-      if constexpr (EPI == EPI_STORE) {
-        static_cast<T*>(ep.out)[o] = from_f32<T>(val * ep.out_scale);
-      } else if constexpr (EPI == EPI_GELU) {
-        static_cast<T*>(ep.out)[o] = from_f32<T>(gelu_tanh(val));
-      } else {  // EPI_RES: h_out = h_in + gate * val
-        float gate = 1.0f;
-        if (ep.gate_row >= 0) {
-          const int ti = (int)ep.div_L.div(row);
-          gate = ep.mod[((size_t)ti * 6 + ep.gate_row) * N + col];
+    for (int r0 = 0; r0 < nrows; r0 += EB) {
+      float val[EB];
+#pragma unroll
+      for (int k = 0; k < EB; ++k) val[k] = stg[min(r0 + k, 127) * EPITCH + lane] + bias;
+      if constexpr (EPI == EPI_RES) {
+        float hv[EB], gv[EB];
+#pragma unroll
+        for (int k = 0; k < EB; ++k) {
+          const int row = rbase + min(r0 + k, nrows - 1);
+          const size_t o = (size_t)row * N + (col_ok ? col : 0);
+          hv[k] = ep.h_in[o];
+          gv[k] = 1.0f;
+          if (ep.gate_row >= 0) {
+            const int ti = (int)ep.div_L.div(row);
+            gv[k] = ep.mod[((size_t)ti * 6 + ep.gate_row) * N + (col_ok ? col : 0)];
+          }
         }
-        ep.h_out[o] = ep.h_in[o] + gate * val;
+#pragma unroll
+        for (int k = 0; k < EB; ++k) {
+          if (r0 + k >= nrows || !col_ok) continue;
+          const size_t o = (size_t)(rbase + r0 + k) * N + col;
+          ep.h_out[o] = hv[k] + gv[k] * val[k];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < EB; ++k) {
+          if (r0 + k >= nrows || !col_ok) continue;
+          const size_t o = (size_t)(rbase + r0 + k) * N + col;
+          if constexpr (EPI == EPI_STORE) {
+            static_cast<T*>(ep.out)[o] = from_f32<T>(val[k] * ep.out_scale);
+          } else {
+            static_cast<T*>(ep.out)[o] = from_f32<T>(gelu_tanh(val[k]));
+          }
+        }
       }
     }
   }
@@ -170,7 +212,6 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
                                              const DevTask* __restrict__ tasks) {
   constexpr int BK = ROWB / sizeof(T);
   __shared__ u32x4 smem[SMEM_BYTES / 16];
-  u32x4(*lds)[(BM + BN) * CPR] = reinterpret_cast<u32x4(*)[(BM + BN) * CPR]>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -193,27 +234,30 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
       const_cast<T*>(A), 0, (int)((size_t)M * K * sizeof(T)), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<T*>(B), 0, (int)((size_t)N * K * sizeof(T)), 0x00020000);
-  // this thread moves 16-byte chunk c of rows r0 + 32 i of each operand tile
-  const int c = tid & 7, r0 = tid >> 3;
-  const int pc = c ^ (r0 & 7);
+  // this thread moves 16-byte chunk c of rows r0 + 64 i (i < 4) of each operand
+  // tile; LDS rows are 64 bytes and chunk c of row r sits at c ^ ((r >> 1) & 3),
+  // so 8 consecutive rows read at one logical chunk hit distinct banks
+  const int c = tid & 3, r0 = tid >> 2;
+  const int pc = c ^ ((r0 >> 1) & 3);
   const uint32_t row_bytes = (uint32_t)K * sizeof(T);
   const uint32_t a_off = (uint32_t)(m0 + r0) * row_bytes + c * 16;
   const uint32_t b_off = (uint32_t)(n0 + r0) * row_bytes + c * 16;
-  const uint32_t step32 = 32u * row_bytes;
-  u32x4 ra_[8], rb_[8];
-  auto fetch = [&](int kt) {
+  const uint32_t step64 = 64u * row_bytes;
+  u32x4 rst[2][8];   // two register sets: operand tiles fetched two stages ahead
+  auto fetch = [&](int set, int kt) {
     const int koff = kt * ROWB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra_[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + i * step32), koff, 0);
-      rb_[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(b_off + i * step32), koff, 0);
+    for (int i = 0; i < 4; ++i) {
+      rst[set][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + i * step64), koff, 0);
+      rst[set][4 + i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(b_off + i * step64), koff, 0);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int set, int buf) {
+    u32x4* st = smem + buf * STAGE_CH;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lds[buf][(r0 + 32 * i) * CPR + pc] = ra_[i];
-      lds[buf][(BM + r0 + 32 * i) * CPR + pc] = rb_[i];
+    for (int i = 0; i < 4; ++i) {
+      st[(r0 + 64 * i) * CPR + pc] = rst[set][i];
+      st[(BM + r0 + 64 * i) * CPR + pc] = rst[set][4 + i];
     }
   };
 
@@ -226,27 +270,92 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int wm = wave >> 1, wn = wave & 1;
+  const int fsw = (l32 >> 1) & 3;
+  u32x4 fr[2][8];   // MFMA fragments of two k-units (A 0..3, B 4..7)
+  auto frags = [&](int set, int buf, int u) {
+    const u32x4* st = smem + buf * STAGE_CH;
+    const int ch = (2 * u + g) ^ fsw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fr[set][i] = st[(wm * 128 + i * 32 + l32) * CPR + ch];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fr[set][4 + j] = st[(BM + wn * 128 + j * 32 + l32) * CPR + ch];
+  };
+  auto mma = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Mfma<T>::unit(acc[i][j], fr[set][i], fr[set][4 + j]);
+  };
+
+  // Pipeline: stage kt is multiplied while stage kt + 1 sits in LDS (its first
+  // fragments are read during the second half of stage kt), stage kt + 2 is
+  // written to LDS and stage kt + 4 is fetched from memory.  One barrier per
+  // stage; a ring of 4 LDS stages keeps writes away from live stages.
   const int nk = K / BK;
-  fetch(0);
-  stash(0);
+  fetch(0, 0);
+  if (nk > 1) fetch(1, 1);
+  stash(0, 0);
+  if (nk > 2) fetch(0, 2);
+  if (nk > 1) stash(1, 1);
+  if (nk > 3) fetch(1, 3);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) fetch(kt + 1);
-#pragma unroll
-    for (int u = 0; u < CPR / 2; ++u) {
-      const int ch = (2 * u + g) ^ (l32 & 7);
-      u32x4 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = lds[buf][(wm * 128 + i * 32 + l32) * CPR + ch];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = lds[buf][(BM + wn * 128 + j * 32 + l32) * CPR + ch];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Mfma<T>::unit(acc[i][j], af[i], bfr[j]);
+  frags(0, 0, 0);
+  // Instruction order inside a stage: memory operations spread between the
+  // MFMAs so that LDS and buffer latencies hide behind matrix work.
+  auto interleave = [&]() {
+    for (int i = 0; i < 8; ++i) {            // unit-1 fragment reads under unit-0 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    if (kt + 1 < nk) stash(buf ^ 1);
+    for (int i = 0; i < 8; ++i) {            // LDS writes of stage kt + 2
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    for (int i = 0; i < 8; ++i) {            // fetch of stage kt + 4
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    for (int i = 0; i < 8; ++i) {            // next stage's unit-0 fragments
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // Steady state, two stages per trip so that the register set of the stage
+  // fetched two ahead (kt & 1) is a compile-time index.
+#define PS_GEMM_STAGE(KT, SET)                                  \
+  {                                                             \
+    const int kt_ = (KT);                                       \
+    frags(1, kt_ & (NSTAGE - 1), 1);                            \
+    mma(0);                                                     \
+    stash(SET, (kt_ + 2) & (NSTAGE - 1));                       \
+    fetch(SET, kt_ + 4);                                        \
+    frags(0, (kt_ + 1) & (NSTAGE - 1), 0);                      \
+    mma(1);                                                     \
+    interleave();                                               \
+    __syncthreads();                                            \
+  }
+  int kt = 0;
+  for (; kt + 5 < nk; kt += 2) {
+    PS_GEMM_STAGE(kt, 0)
+    PS_GEMM_STAGE(kt + 1, 1)
+  }
+#undef PS_GEMM_STAGE
+  // drain: the last stages (fewer than 6 left), with the guards
+  for (; kt < nk; ++kt) {
+    const int cur = kt & (NSTAGE - 1);
+    frags(1, cur, 1);
+    mma(0);
+    if (kt + 2 < nk) {
+      if (kt & 1) {
+        stash(1, (kt + 2) & (NSTAGE - 1));
+        if (kt + 4 < nk) fetch(1, kt + 4);
+      } else {
+        stash(0, (kt + 2) & (NSTAGE - 1));
+        if (kt + 4 < nk) fetch(0, kt + 4);
+      }
+    }
+    if (kt + 1 < nk) frags(0, (kt + 1) & (NSTAGE - 1), 0);
+    mma(1);
     __syncthreads();
   }
 
