@@ -141,13 +141,13 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, PoolGeo pg, const DevTask* 
     for (int i = 0; i < KLD; ++i) {
       const int e = tid + NT * i;
       const int row = e / KCH, c = e % KCH;
-      ks[buf][row * KCH + (c ^ (row & 7))] = kr[i];
+      ks[buf][row * KCH + (c ^ lds_swz<KCH>(row))] = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int e = tid + NT * i;
       const int f = e / VCH, c = e % VCH;
-      vs[buf][f * VCH + (c ^ (f & 7))] = vr[i];
+      vs[buf][f * VCH + (c ^ lds_swz<VCH>(f))] = vr[i];
     }
   };
 
@@ -176,7 +176,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, PoolGeo pg, const DevTask* 
       s[t] = negm;
 #pragma unroll
       for (int u = 0; u < NU_QK; ++u) {
-        const u32x4 kf = ks[buf][(t * 32 + l32) * KCH + ((2 * u + g) ^ (l32 & 7))];
+        const u32x4 kf = ks[buf][(t * 32 + l32) * KCH + ((2 * u + g) ^ lds_swz<KCH>(l32))];
         Mfma<T>::unit(s[t], kf, qf[u]);
       }
     }
@@ -245,7 +245,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, PoolGeo pg, const DevTask* 
 #pragma unroll
       for (int i = 0; i < HD / 32; ++i) {
         const int f = i * 32 + l32;
-        const u32x4 vf = vs[buf][f * VCH + ((2 * u + g) ^ (f & 7))];
+        const u32x4 vf = vs[buf][f * VCH + ((2 * u + g) ^ lds_swz<VCH>(f))];
         Mfma<T>::unit(o[i], vf, pf);
       }
     }

@@ -52,6 +52,22 @@ struct Mfma<float> {
   }
 };
 
+// XOR swizzle of 16-byte chunks in an LDS row holding CH chunks, chosen so
+// that MFMA fragment reads -- consecutive rows at one logical chunk -- hit
+// distinct banks both when 8 lanes share a 128-byte bank cycle and when 16
+// lanes share a 256-byte one.
+template <int CH>
+__device__ __forceinline__ int lds_swz(int row) {
+  if constexpr (CH >= 16) {
+    return row & 15;
+  } else if constexpr (CH == 8) {
+    return (row & 7) ^ ((row >> 3) & 1);
+  } else {
+    static_assert(CH == 4, "unsupported LDS row width");
+    return ((row >> 1) ^ (row >> 3)) & 3;
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ T from_f32(float x);
 template <>

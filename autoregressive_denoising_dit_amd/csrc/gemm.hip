@@ -7,12 +7,13 @@
 // share one weight pass: AREX article on the PhysisServe report, section
 // "三层设计", layer 2).
 //
-// Tiling: 256 x 256 macro tile, 128 bytes of K per stage (64 bf16 / 32 fp32),
-// 4 waves in a 2 x 2 grid, each owning a 128 x 128 sub-tile = 4 x 4 MFMA
-// 32x32 accumulators.  Operand tiles are double-buffered in LDS (2 x 64 KB)
-// with a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) so that the MFMA
-// fragment reads of 32 consecutive rows hit distinct banks.  The next K stage
-// is fetched into registers while the current one is multiplied.
+// Tiling: 256 x 256 macro tile, 4 waves in a 2 x 2 grid, each owning a
+// 128 x 128 sub-tile = 4 x 4 MFMA 32x32 accumulators (in AGPRs).  K advances
+// in stages of 64 bytes per row (32 bf16 / 16 fp32) through a ring of 4 LDS
+// stages; operand chunks are XOR-swizzled so that fragment reads of
+// consecutive rows hit distinct banks.  Stage kt is multiplied while the
+// first fragments of stage kt + 1 are read, stage kt + 2 is written to LDS
+// and stage kt + 4 is fetched into registers.
 //
 // Tile order: the linear workgroup id is first remapped so that consecutive
 // ids land on the same XCD (the dispatcher deals workgroups to the 8 XCDs
@@ -35,6 +36,28 @@ constexpr int STAGE_CH = (BM + BN) * CPR;               // 16-byte chunks per st
 constexpr int OPER_BYTES = NSTAGE * STAGE_CH * 16;      // 4 x 32 KB
 constexpr int STAGE_BYTES = 4 * 128 * EPITCH * 4;      // 4 waves x 128 rows x pitch
 constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes per lane from a raw buffer straight into LDS at lds_addr + 16 * lane.
+// Written as inline assembly so that the compiler does not treat every later
+// LDS read as dependent on it (it would wait for all copies in flight); the
+// kernel orders these copies itself with vm_wait + barriers.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// s_waitcnt vmcnt(n) for n in {0, 8, 16} (memory operations still in flight).
+__device__ __forceinline__ void vm_wait(int n) {
+  if (n >= 16) {
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  } else if (n >= 8) {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
 
 __device__ __forceinline__ int xcd_remap(int id, int total) {
   const int full = (total / 8) * 8;
@@ -228,37 +251,34 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const int tn = (pid % per_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // Operand fetch through buffer resources: rows past M (or N) lie past the
-  // resource's end and read as zero, so ragged tiles need no clamping.
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(A), 0, (int)((size_t)M * K * sizeof(T)), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(B), 0, (int)((size_t)N * K * sizeof(T)), 0x00020000);
-  // this thread moves 16-byte chunk c of rows r0 + 64 i (i < 4) of each operand
-  // tile; LDS rows are 64 bytes and chunk c of row r sits at c ^ ((r >> 1) & 3),
-  // so 8 consecutive rows read at one logical chunk hit distinct banks
-  const int c = tid & 3, r0 = tid >> 2;
-  const int pc = c ^ ((r0 >> 1) & 3);
+  // Operands stream from memory straight into LDS (buffer_load ... lds): each
+  // instruction moves 64 lanes x 16 bytes into one contiguous 1 KB block =
+  // 16 rows of a stage.  Rows past M (or N) lie past the buffer resource's end
+  // and arrive as zeros, so ragged tiles need no clamping.  The chunk a lane
+  // fetches is chosen so that the block lands already swizzled.
+  const uint64_t a_base = (uint64_t)(uintptr_t)A, b_base = (uint64_t)(uintptr_t)B;
+  const i32x4 rsa = {(int)(uint32_t)a_base, (int)(uint32_t)(a_base >> 32), (int)((size_t)M * K * sizeof(T)),
+                     0x00020000};
+  const i32x4 rsb = {(int)(uint32_t)b_base, (int)(uint32_t)(b_base >> 32), (int)((size_t)N * K * sizeof(T)),
+                     0x00020000};
   const uint32_t row_bytes = (uint32_t)K * sizeof(T);
-  const uint32_t a_off = (uint32_t)(m0 + r0) * row_bytes + c * 16;
-  const uint32_t b_off = (uint32_t)(n0 + r0) * row_bytes + c * 16;
-  const uint32_t step64 = 64u * row_bytes;
-  u32x4 rst[2][8];   // two register sets: operand tiles fetched two stages ahead
-  auto fetch = [&](int set, int kt) {
-    const int koff = kt * ROWB;
+  uint32_t voa[4], vob[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rst[set][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(a_off + i * step64), koff, 0);
-      rst[set][4 + i] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)(b_off + i * step64), koff, 0);
-    }
-  };
-  auto stash = [&](int set, int buf) {
-    u32x4* st = smem + buf * STAGE_CH;
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 16 + (lane >> 2);
+    const int cl = (lane & 3) ^ lds_swz<CPR>(row);
+    voa[i] = (uint32_t)(m0 + row) * row_bytes + cl * 16;
+    vob[i] = (uint32_t)(n0 + row) * row_bytes + cl * 16;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t wblk = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 4 * 1024);
+  auto dma_stage = [&](int kt) {
+    const uint32_t dst = lds0 + (kt & (NSTAGE - 1)) * (STAGE_CH * 16) + wblk;
+    const uint32_t koff = (uint32_t)kt * ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st[(r0 + 64 * i) * CPR + pc] = rst[set][i];
-      st[(BM + r0 + 64 * i) * CPR + pc] = rst[set][4 + i];
-    }
+    for (int i = 0; i < 4; ++i) lds_dma16(rsa, voa[i], koff, dst + i * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(rsb, vob[i], koff, dst + BM * ROWB + i * 1024);
   };
 
   f32x16 acc[4][4];
@@ -270,7 +290,7 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int wm = wave >> 1, wn = wave & 1;
-  const int fsw = (l32 >> 1) & 3;
+  const int fsw = lds_swz<CPR>(l32);
   u32x4 fr[2][8];   // MFMA fragments of two k-units (A 0..3, B 4..7)
   auto frags = [&](int set, int buf, int u) {
     const u32x4* st = smem + buf * STAGE_CH;
@@ -286,78 +306,38 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
 #pragma unroll
       for (int j = 0; j < 4; ++j) Mfma<T>::unit(acc[i][j], fr[set][i], fr[set][4 + j]);
   };
-
-  // Pipeline: stage kt is multiplied while stage kt + 1 sits in LDS (its first
-  // fragments are read during the second half of stage kt), stage kt + 2 is
-  // written to LDS and stage kt + 4 is fetched from memory.  One barrier per
-  // stage; a ring of 4 LDS stages keeps writes away from live stages.
-  const int nk = K / BK;
-  fetch(0, 0);
-  if (nk > 1) fetch(1, 1);
-  stash(0, 0);
-  if (nk > 2) fetch(0, 2);
-  if (nk > 1) stash(1, 1);
-  if (nk > 3) fetch(1, 3);
-  __syncthreads();
-  frags(0, 0, 0);
-  // Instruction order inside a stage: memory operations spread between the
-  // MFMAs so that LDS and buffer latencies hide behind matrix work.
+  // Instruction order: LDS fragment reads and the memory-to-LDS copies spread
+  // between the MFMAs so that their latencies hide behind matrix work.
   auto interleave = [&]() {
-    for (int i = 0; i < 8; ++i) {            // unit-1 fragment reads under unit-0 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    for (int i = 0; i < 8; ++i) {            // LDS writes of stage kt + 2
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
-    for (int i = 0; i < 8; ++i) {            // fetch of stage kt + 4
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    for (int i = 0; i < 8; ++i) {            // next stage's unit-0 fragments
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  // Steady state, two stages per trip so that the register set of the stage
-  // fetched two ahead (kt & 1) is a compile-time index.
-#define PS_GEMM_STAGE(KT, SET)                                  \
-  {                                                             \
-    const int kt_ = (KT);                                       \
-    frags(1, kt_ & (NSTAGE - 1), 1);                            \
-    mma(0);                                                     \
-    stash(SET, (kt_ + 2) & (NSTAGE - 1));                       \
-    fetch(SET, kt_ + 4);                                        \
-    frags(0, (kt_ + 1) & (NSTAGE - 1), 0);                      \
-    mma(1);                                                     \
-    interleave();                                               \
-    __syncthreads();                                            \
-  }
-  int kt = 0;
-  for (; kt + 5 < nk; kt += 2) {
-    PS_GEMM_STAGE(kt, 0)
-    PS_GEMM_STAGE(kt + 1, 1)
-  }
-#undef PS_GEMM_STAGE
-  // drain: the last stages (fewer than 6 left), with the guards
-  for (; kt < nk; ++kt) {
-    const int cur = kt & (NSTAGE - 1);
-    frags(1, cur, 1);
+
+  // Pipeline over stages of 64 bytes of K: stage kt + 3 is copied into the
+  // LDS ring (4 stages) while stage kt is multiplied; the first fragments of
+  // stage kt + 1 are read during the second half of stage kt.  One barrier per
+  // stage, after which stage kt + 1 is complete in LDS for every wave.
+  const int nk = K / BK;
+  for (int s = 0; s < 3 && s < nk; ++s) dma_stage(s);
+  vm_wait(8 * (min(3, nk) - 1));
+  __syncthreads();
+  frags(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    frags(1, kt & (NSTAGE - 1), 1);
     mma(0);
-    if (kt + 2 < nk) {
-      if (kt & 1) {
-        stash(1, (kt + 2) & (NSTAGE - 1));
-        if (kt + 4 < nk) fetch(1, kt + 4);
-      } else {
-        stash(0, (kt + 2) & (NSTAGE - 1));
-        if (kt + 4 < nk) fetch(0, kt + 4);
-      }
+    interleave();
+    if (kt + 3 < nk) dma_stage(kt + 3);
+    if (kt + 1 < nk) {
+      vm_wait(8 * (min(kt + 3, nk - 1) - (kt + 1)));
+      __syncthreads();
+      frags(0, (kt + 1) & (NSTAGE - 1), 0);
     }
-    if (kt + 1 < nk) frags(0, (kt + 1) & (NSTAGE - 1), 0);
     mma(1);
-    __syncthreads();
+    interleave();
   }
+  __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
   // The accumulators go through LDS, 64 columns at a time (row pitch 65
