@@ -486,16 +486,21 @@ extern "C" ps_status ps_context_set(ps_kv_pool* p, const ps_block* b, int32_t st
   ep.d_shift = bd.head_dim == 128 ? 7 : 6;
   const int D = bd.hidden;
   if (bd.dtype == PS_BF16)
-    PS_HIP(launch_gemm<bf16>(EPI_CTX_KV, static_cast<const bf16*>(ctx), static_cast<const bf16*>(bd.wkv2), n_ctx,
-                             2 * D, D, ep, nullptr, hs));
+    PS_HIP(launch_gemm<bf16>(EPI_CTX_KV, static_cast<const bf16*>(ctx), D, static_cast<const bf16*>(bd.wkv2),
+                             n_ctx, 2 * D, D, ep, nullptr, hs));
   else
-    PS_HIP(launch_gemm<float>(EPI_CTX_KV, static_cast<const float*>(ctx), static_cast<const float*>(bd.wkv2), n_ctx,
-                              2 * D, D, ep, nullptr, hs));
+    PS_HIP(launch_gemm<float>(EPI_CTX_KV, static_cast<const float*>(ctx), D, static_cast<const float*>(bd.wkv2),
+                              n_ctx, 2 * D, D, ep, nullptr, hs));
   p->ctx_len[cr] = n_ctx;
   return PS_OK;
 }
 
 // ------------------------------------------------------------------ stage
+// Row stride of the activation buffers that feed a GEMM as its A operand:
+// padded by 64 elements so that the rows of a tile do not all begin on the
+// same memory channel (a dense stride of 5120 or 13824 bf16 elements does).
+static int act_ld(int cols) { return cols + 64; }
+
 template <typename T>
 static ps_status run_stage(ps_kv_pool* p, const ps_block* b, const DevTask* tt, int n, const float* mod,
                            const float2* rope_f, const float* h_in, float* h_out, hipStream_t hs) {
@@ -510,17 +515,19 @@ static ps_status run_stage(ps_kv_pool* p, const ps_block* b, const DevTask* tt, 
   const T* W = nullptr;
 
   // self-attention branch
-  PS_TRACED("ln1", (launch_layernorm<T>(h_in, y, M, D, mod, 0, 1, L, hs)));
+  const int ldy = act_ld(D), ldu = act_ld(F);
+  PS_TRACED("ln1", (launch_layernorm<T>(h_in, y, ldy, M, D, mod, 0, 1, L, hs)));
   EpiArgs e1;
   e1.bias = bd.bqkv;
   e1.out = q;
+  e1.ldo = D;
   e1.out_scale = qscale;
   e1.rope_f = rope_f;
   e1.pool = pg;
   e1.d_shift = bd.head_dim == 128 ? 7 : 6;
   W = static_cast<const T*>(bd.wqkv);
-  PS_TRACED("qkv", (launch_gemm<T>(EPI_QKV, y, W, M, 3 * D, D, e1, tt, hs)));
-  PS_TRACED("attn_self", (launch_attention<T>(false, q, a, pg, tt, n, hs)));
+  PS_TRACED("qkv", (launch_gemm<T>(EPI_QKV, y, ldy, W, M, 3 * D, D, e1, tt, hs)));
+  PS_TRACED("attn_self", (launch_attention<T>(false, q, a, ldy, pg, tt, n, hs)));
   EpiArgs e2;
   e2.bias = bd.bo;
   e2.h_in = h_in;
@@ -529,30 +536,32 @@ static ps_status run_stage(ps_kv_pool* p, const ps_block* b, const DevTask* tt, 
   e2.gate_row = 2;
   e2.L = L;
   e2.div_L = FastDiv((uint32_t)L);
-  PS_TRACED("o_proj", (launch_gemm<T>(EPI_RES, a, static_cast<const T*>(bd.wo), M, D, D, e2, tt, hs)));
+  PS_TRACED("o_proj", (launch_gemm<T>(EPI_RES, a, ldy, static_cast<const T*>(bd.wo), M, D, D, e2, tt, hs)));
 
   // cross-attention branch
-  PS_TRACED("ln2", (launch_layernorm<T>(h_out, y, M, D, nullptr, -1, -1, L, hs)));
+  PS_TRACED("ln2", (launch_layernorm<T>(h_out, y, ldy, M, D, nullptr, -1, -1, L, hs)));
   EpiArgs e3;
   e3.bias = bd.bq2;
   e3.out = q;
+  e3.ldo = D;
   e3.out_scale = qscale;
-  PS_TRACED("xq_proj", (launch_gemm<T>(EPI_STORE, y, static_cast<const T*>(bd.wq2), M, D, D, e3, tt, hs)));
-  PS_TRACED("attn_cross", (launch_attention<T>(true, q, a, pg, tt, n, hs)));
+  PS_TRACED("xq_proj", (launch_gemm<T>(EPI_STORE, y, ldy, static_cast<const T*>(bd.wq2), M, D, D, e3, tt, hs)));
+  PS_TRACED("attn_cross", (launch_attention<T>(true, q, a, ldy, pg, tt, n, hs)));
   EpiArgs e4;
   e4.bias = bd.bo2;
   e4.h_in = h_out;
   e4.h_out = h_out;
   e4.L = L;
   e4.div_L = FastDiv((uint32_t)L);
-  PS_TRACED("xo_proj", (launch_gemm<T>(EPI_RES, a, static_cast<const T*>(bd.wo2), M, D, D, e4, tt, hs)));
+  PS_TRACED("xo_proj", (launch_gemm<T>(EPI_RES, a, ldy, static_cast<const T*>(bd.wo2), M, D, D, e4, tt, hs)));
 
   // FFN branch
-  PS_TRACED("ln3", (launch_layernorm<T>(h_out, y, M, D, mod, 3, 4, L, hs)));
+  PS_TRACED("ln3", (launch_layernorm<T>(h_out, y, ldy, M, D, mod, 3, 4, L, hs)));
   EpiArgs e5;
   e5.bias = bd.b1;
   e5.out = u;
-  PS_TRACED("ffn1", (launch_gemm<T>(EPI_GELU, y, static_cast<const T*>(bd.w1), M, F, D, e5, tt, hs)));
+  e5.ldo = ldu;
+  PS_TRACED("ffn1", (launch_gemm<T>(EPI_GELU, y, ldy, static_cast<const T*>(bd.w1), M, F, D, e5, tt, hs)));
   EpiArgs e6;
   e6.bias = bd.b2;
   e6.h_in = h_out;
@@ -561,7 +570,7 @@ static ps_status run_stage(ps_kv_pool* p, const ps_block* b, const DevTask* tt, 
   e6.gate_row = 5;
   e6.L = L;
   e6.div_L = FastDiv((uint32_t)L);
-  PS_TRACED("ffn2", (launch_gemm<T>(EPI_RES, u, static_cast<const T*>(bd.w2), M, D, F, e6, tt, hs)));
+  PS_TRACED("ffn2", (launch_gemm<T>(EPI_RES, u, ldu, static_cast<const T*>(bd.w2), M, D, F, e6, tt, hs)));
   return PS_OK;
 }
 
@@ -636,10 +645,10 @@ extern "C" ps_status ps_stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_em
   ps_status st;
   if ((st = p->ws_mod.reserve(sizeof(float) * n * 6 * (size_t)D))) return st;
   if ((st = p->ws_rope.reserve(sizeof(float2) * n * pd.frames * (size_t)(p->seg_f / 2) + 16))) return st;
-  if ((st = p->ws_y.reserve(M * D * es))) return st;
+  if ((st = p->ws_y.reserve(M * act_ld(D) * es))) return st;
   if ((st = p->ws_q.reserve(M * D * es))) return st;
-  if ((st = p->ws_a.reserve(M * D * es))) return st;
-  if ((st = p->ws_u.reserve(M * F * es))) return st;
+  if ((st = p->ws_a.reserve(M * act_ld(D) * es))) return st;
+  if ((st = p->ws_u.reserve(M * act_ld(F) * es))) return st;
   if ((st = p->ws_tasks.reserve(sizeof(DevTask) * PS_MAX_TASKS))) return st;
 
   // timestep embeddings (cached per distinct t)

@@ -55,8 +55,8 @@ __device__ __forceinline__ int perm16(int r) {
 
 template <typename T, int HD>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
-k_attn(const T* __restrict__ q, T* __restrict__ out, PoolGeo pg, const DevTask* __restrict__ tasks, int cross,
-       int n_qt, int n_tasks) {
+k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const DevTask* __restrict__ tasks,
+       int cross, int n_qt, int n_tasks) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KCH = HD / VEC;     // 16-byte chunks per K row
   constexpr int VCH = KT / VEC;     // 16-byte chunks per V^T row
@@ -257,7 +257,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, PoolGeo pg, const DevTask* 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   if (qi < L) {
-    T* orow = out + ((size_t)task * L + qi) * D + (size_t)h * HD;
+    T* orow = out + ((size_t)task * L + qi) * ldo + (size_t)h * HD;
 #pragma unroll
     for (int i = 0; i < HD / 32; ++i)
 #pragma unroll
@@ -281,23 +281,23 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, PoolGeo pg, const DevTask* 
 }  // namespace
 
 template <typename T>
-hipError_t launch_attention(bool cross, const T* q, T* out, const PoolGeo& pg, const DevTask* tt,
+hipError_t launch_attention(bool cross, const T* q, T* out, int ldo, const PoolGeo& pg, const DevTask* tt,
                             int n_tasks, hipStream_t s) {
   const int n_qt = (pg.L + QT - 1) / QT;
   dim3 grid(n_qt * pg.H * n_tasks), block(NT);
   if (pg.d == 128) {
-    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, q, out, pg, tt, cross ? 1 : 0, n_qt, n_tasks);
+    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, q, out, ldo, pg, tt, cross ? 1 : 0, n_qt, n_tasks);
   } else if (pg.d == 64) {
-    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, q, out, pg, tt, cross ? 1 : 0, n_qt, n_tasks);
+    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, q, out, ldo, pg, tt, cross ? 1 : 0, n_qt, n_tasks);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template hipError_t launch_attention<bf16>(bool, const bf16*, bf16*, const PoolGeo&, const DevTask*,
+template hipError_t launch_attention<bf16>(bool, const bf16*, bf16*, int, const PoolGeo&, const DevTask*,
                                            int, hipStream_t);
-template hipError_t launch_attention<float>(bool, const float*, float*, const PoolGeo&,
+template hipError_t launch_attention<float>(bool, const float*, float*, int, const PoolGeo&,
                                             const DevTask*, int, hipStream_t);
 
 }  // namespace ps

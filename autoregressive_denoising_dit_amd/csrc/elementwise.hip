@@ -28,8 +28,8 @@ template <>
 struct VecF<2> { typedef float __attribute__((ext_vector_type(2))) type; };
 
 template <typename T, int VW, int MAXI>
-__global__ void __launch_bounds__(256) k_layernorm(const float* __restrict__ h, T* __restrict__ y, int M,
-                                                   int D, const float* __restrict__ mod, int shift_row,
+__global__ void __launch_bounds__(256) k_layernorm(const float* __restrict__ h, T* __restrict__ y, int ldy,
+                                                   int M, int D, const float* __restrict__ mod, int shift_row,
                                                    int scale_row, int L) {
   typedef typename VecF<VW>::type vf;
   const int lane = threadIdx.x & 63;
@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(256) k_layernorm(const float* __restrict__ h, 
     shift = mod + ((size_t)ti * 6 + shift_row) * D;
     scale = mod + ((size_t)ti * 6 + scale_row) * D;
   }
-  T* yr = y + (size_t)row * D;
+  T* yr = y + (size_t)row * ldy;
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     if (i < ni) {
@@ -230,21 +230,21 @@ __global__ void k_entry_fetch(const T* entry, T* k, T* v, int n, int stride, int
 }  // namespace
 
 template <typename T>
-hipError_t launch_layernorm(const float* h, T* y, int M, int D, const float* mod, int shift_row,
+hipError_t launch_layernorm(const float* h, T* y, int ldy, int M, int D, const float* mod, int shift_row,
                             int scale_row, int L, hipStream_t s) {
   dim3 grid((M + 3) / 4), block(256);
   if (D % 256 == 0 && D <= 8192) {
-    hipLaunchKernelGGL((k_layernorm<T, 4, 32>), grid, block, 0, s, h, y, M, D, mod, shift_row, scale_row, L);
+    hipLaunchKernelGGL((k_layernorm<T, 4, 32>), grid, block, 0, s, h, y, ldy, M, D, mod, shift_row, scale_row, L);
   } else if (D % 128 == 0 && D <= 8192) {
-    hipLaunchKernelGGL((k_layernorm<T, 2, 64>), grid, block, 0, s, h, y, M, D, mod, shift_row, scale_row, L);
+    hipLaunchKernelGGL((k_layernorm<T, 2, 64>), grid, block, 0, s, h, y, ldy, M, D, mod, shift_row, scale_row, L);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
-template hipError_t launch_layernorm<bf16>(const float*, bf16*, int, int, const float*, int, int, int,
+template hipError_t launch_layernorm<bf16>(const float*, bf16*, int, int, int, const float*, int, int, int,
                                            hipStream_t);
-template hipError_t launch_layernorm<float>(const float*, float*, int, int, const float*, int, int, int,
+template hipError_t launch_layernorm<float>(const float*, float*, int, int, int, const float*, int, int, int,
                                             hipStream_t);
 
 hipError_t launch_modulation(const float* e_cache, const int* e_rows_host, const float* tmod, float* mod,

@@ -28,12 +28,12 @@ namespace ps {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, ROWB = 64, NT = 256;
-constexpr int CPR = ROWB / 16;  // 16-byte chunks per LDS row (4)
-constexpr int NSTAGE = 4;       // LDS ring of operand stages
+constexpr int BM = 256, BN = 256, ROWB = 128, NT = 256;
+constexpr int CPR = ROWB / 16;  // 16-byte chunks per LDS row (8)
+constexpr int NSTAGE = 2;       // LDS stages of operands
 constexpr int EPITCH = 65;      // fp32 row pitch of the epilogue staging (64 columns + 1)
 constexpr int STAGE_CH = (BM + BN) * CPR;               // 16-byte chunks per stage
-constexpr int OPER_BYTES = NSTAGE * STAGE_CH * 16;      // 4 x 32 KB
+constexpr int OPER_BYTES = NSTAGE * STAGE_CH * 16;      // 2 x 64 KB
 constexpr int STAGE_BYTES = 4 * 128 * EPITCH * 4;      // 4 waves x 128 rows x pitch
 constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
 
@@ -217,7 +217,7 @@ __device__ __forceinline__ void epilogue_half(const float* stg, int rbase, int c
 #pragma unroll
         for (int k = 0; k < EB; ++k) {
           if (r0 + k >= nrows || !col_ok) continue;
-          const size_t o = (size_t)(rbase + r0 + k) * N + col;
+          const size_t o = (size_t)(rbase + r0 + k) * ep.ldo + col;
           if constexpr (EPI == EPI_STORE) {
             static_cast<T*>(ep.out)[o] = from_f32<T>(val[k] * ep.out_scale);
           } else {
@@ -231,7 +231,7 @@ __device__ __forceinline__ void epilogue_half(const float* stg, int rbase, int c
 
 template <typename T, int EPI>
 __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* __restrict__ B,
-                                             int M, int N, int K, EpiArgs ep,
+                                             int M, int N, int K, int lda, EpiArgs ep,
                                              const DevTask* __restrict__ tasks) {
   constexpr int BK = ROWB / sizeof(T);
   __shared__ u32x4 smem[SMEM_BYTES / 16];
@@ -253,32 +253,35 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
 
   // Operands stream from memory straight into LDS (buffer_load ... lds): each
   // instruction moves 64 lanes x 16 bytes into one contiguous 1 KB block =
-  // 16 rows of a stage.  Rows past M (or N) lie past the buffer resource's end
-  // and arrive as zeros, so ragged tiles need no clamping.  The chunk a lane
-  // fetches is chosen so that the block lands already swizzled.
+  // 8 rows of a stage (128 bytes of K each: whole cache lines).  Rows past M
+  // (or N) lie past the buffer resource's end and arrive as zeros, so ragged
+  // tiles need no clamping.  The chunk a lane fetches is chosen so that the
+  // block lands already swizzled.  A's row stride is lda elements (the
+  // activation buffers are padded so that rows do not all start on the same
+  // memory channel); B is dense.
   const uint64_t a_base = (uint64_t)(uintptr_t)A, b_base = (uint64_t)(uintptr_t)B;
-  const i32x4 rsa = {(int)(uint32_t)a_base, (int)(uint32_t)(a_base >> 32), (int)((size_t)M * K * sizeof(T)),
+  const i32x4 rsa = {(int)(uint32_t)a_base, (int)(uint32_t)(a_base >> 32), (int)((size_t)M * lda * sizeof(T)),
                      0x00020000};
   const i32x4 rsb = {(int)(uint32_t)b_base, (int)(uint32_t)(b_base >> 32), (int)((size_t)N * K * sizeof(T)),
                      0x00020000};
-  const uint32_t row_bytes = (uint32_t)K * sizeof(T);
-  uint32_t voa[4], vob[4];
+  const uint32_t a_row = (uint32_t)lda * sizeof(T), b_row = (uint32_t)K * sizeof(T);
+  uint32_t voa[8], vob[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wave * 4 + i) * 16 + (lane >> 2);
-    const int cl = (lane & 3) ^ lds_swz<CPR>(row);
-    voa[i] = (uint32_t)(m0 + row) * row_bytes + cl * 16;
-    vob[i] = (uint32_t)(n0 + row) * row_bytes + cl * 16;
+  for (int i = 0; i < 8; ++i) {
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
+    const int cl = (lane & 7) ^ lds_swz<CPR>(row);
+    voa[i] = (uint32_t)(m0 + row) * a_row + cl * 16;
+    vob[i] = (uint32_t)(n0 + row) * b_row + cl * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const uint32_t wblk = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 4 * 1024);
+  const uint32_t wblk = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 8 * 1024);
   auto dma_stage = [&](int kt) {
     const uint32_t dst = lds0 + (kt & (NSTAGE - 1)) * (STAGE_CH * 16) + wblk;
     const uint32_t koff = (uint32_t)kt * ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(rsa, voa[i], koff, dst + i * 1024);
+    for (int i = 0; i < 8; ++i) lds_dma16(rsa, voa[i], koff, dst + i * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(rsb, vob[i], koff, dst + BM * ROWB + i * 1024);
+    for (int i = 0; i < 8; ++i) lds_dma16(rsb, vob[i], koff, dst + BM * ROWB + i * 1024);
   };
 
   f32x16 acc[4][4];
@@ -315,24 +318,37 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
     }
   };
 
-  // Pipeline over stages of 64 bytes of K: stage kt + 3 is copied into the
-  // LDS ring (4 stages) while stage kt is multiplied; the first fragments of
-  // stage kt + 1 are read during the second half of stage kt.  One barrier per
-  // stage, after which stage kt + 1 is complete in LDS for every wave.
+  // Pipeline over stages of 128 bytes of K (four MFMA k-units), two LDS
+  // buffers.  Stage kt + 1 is copied in while stage kt is multiplied; the
+  // barrier sits before the last k-unit of stage kt, so that the first
+  // fragments of stage kt + 1 are read while that unit's MFMAs run, and the
+  // copy of stage kt + 2 (into the buffer just finished) starts right after it.
   const int nk = K / BK;
-  for (int s = 0; s < 3 && s < nk; ++s) dma_stage(s);
-  vm_wait(8 * (min(3, nk) - 1));
+  dma_stage(0);
+  if (nk > 1) {
+    dma_stage(1);
+    vm_wait(16);
+  } else {
+    vm_wait(0);
+  }
   __syncthreads();
   frags(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    frags(1, kt & (NSTAGE - 1), 1);
+    const int buf = kt & 1;
+    frags(1, buf, 1);
     mma(0);
     interleave();
-    if (kt + 3 < nk) dma_stage(kt + 3);
+    frags(0, buf, 2);
+    mma(1);
+    interleave();
+    frags(1, buf, 3);
+    mma(0);
+    interleave();
     if (kt + 1 < nk) {
-      vm_wait(8 * (min(kt + 3, nk - 1) - (kt + 1)));
+      vm_wait(0);
       __syncthreads();
-      frags(0, (kt + 1) & (NSTAGE - 1), 0);
+      if (kt + 2 < nk) dma_stage(kt + 2);
+      frags(0, buf ^ 1, 0);
     }
     mma(1);
     interleave();
@@ -364,29 +380,29 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
 }  // namespace
 
 template <typename T>
-hipError_t launch_gemm(int epi, const T* A, const T* B, int M, int N, int K, const EpiArgs& ep,
+hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, int K, const EpiArgs& ep,
                        const DevTask* tt, hipStream_t s) {
   // 32-bit buffer offsets: every operand byte (plus one tile of overrun) must be addressable
   const uint64_t lim = 1ull << 32;
-  if ((uint64_t)(M + BM) * K * sizeof(T) >= lim || (uint64_t)(N + BN) * K * sizeof(T) >= lim ||
-      K % (ROWB / (int)sizeof(T)) != 0 || M <= 0 || N <= 0)
+  if ((uint64_t)(M + BM) * lda * sizeof(T) >= lim || (uint64_t)(N + BN) * K * sizeof(T) >= lim ||
+      K % (ROWB / (int)sizeof(T)) != 0 || M <= 0 || N <= 0 || lda < K || (lda * sizeof(T)) % 16 != 0)
     return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid(tiles), block(NT);
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((k_gemm<T, EPI_QKV>), grid, block, 0, s, A, B, M, N, K, ep, tt); break;
-    case EPI_CTX_KV: hipLaunchKernelGGL((k_gemm<T, EPI_CTX_KV>), grid, block, 0, s, A, B, M, N, K, ep, tt); break;
-    case EPI_STORE: hipLaunchKernelGGL((k_gemm<T, EPI_STORE>), grid, block, 0, s, A, B, M, N, K, ep, tt); break;
-    case EPI_GELU: hipLaunchKernelGGL((k_gemm<T, EPI_GELU>), grid, block, 0, s, A, B, M, N, K, ep, tt); break;
-    case EPI_RES: hipLaunchKernelGGL((k_gemm<T, EPI_RES>), grid, block, 0, s, A, B, M, N, K, ep, tt); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm<T, EPI_QKV>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
+    case EPI_CTX_KV: hipLaunchKernelGGL((k_gemm<T, EPI_CTX_KV>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
+    case EPI_STORE: hipLaunchKernelGGL((k_gemm<T, EPI_STORE>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
+    case EPI_GELU: hipLaunchKernelGGL((k_gemm<T, EPI_GELU>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
+    case EPI_RES: hipLaunchKernelGGL((k_gemm<T, EPI_RES>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template hipError_t launch_gemm<bf16>(int, const bf16*, const bf16*, int, int, int, const EpiArgs&,
+template hipError_t launch_gemm<bf16>(int, const bf16*, int, const bf16*, int, int, int, const EpiArgs&,
                                       const DevTask*, hipStream_t);
-template hipError_t launch_gemm<float>(int, const float*, const float*, int, int, int, const EpiArgs&,
+template hipError_t launch_gemm<float>(int, const float*, int, const float*, int, int, int, const EpiArgs&,
                                        const DevTask*, hipStream_t);
 
 int gemm_k_step(int dtype) { return dtype == PS_BF16 ? ROWB / 2 : ROWB / 4; }

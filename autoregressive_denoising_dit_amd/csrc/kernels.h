@@ -17,6 +17,7 @@ enum Epi {
 struct EpiArgs {
   const float* bias = nullptr;
   void* out = nullptr;
+  int ldo = 0;                    // row stride of out (elements)
   float out_scale = 1.0f;
   const float* h_in = nullptr;
   float* h_out = nullptr;
@@ -34,7 +35,7 @@ struct EpiArgs {
 hipError_t launch_put_tasks(const TaskTable& tt, DevTask* dst, hipStream_t s);
 
 template <typename T>
-hipError_t launch_gemm(int epi, const T* A, const T* B, int M, int N, int K, const EpiArgs& ep,
+hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, int K, const EpiArgs& ep,
                        const DevTask* tasks, hipStream_t s);
 int gemm_k_step(int dtype);
 
@@ -44,13 +45,13 @@ int gemm_k_step(int dtype);
 // q: [n_tasks * L, H * d] compute dtype, already multiplied by log2(e)/sqrt(d).
 // out: [n_tasks * L, H * d] compute dtype.
 template <typename T>
-hipError_t launch_attention(bool cross, const T* q, T* out, const PoolGeo& pg, const DevTask* tasks,
+hipError_t launch_attention(bool cross, const T* q, T* out, int ldo, const PoolGeo& pg, const DevTask* tasks,
                             int n_tasks, hipStream_t s);
 
 // y = LN(h) * (1 + mod[task][scale_row]) + mod[task][shift_row]  (rows >= 0),
 // or plain LN(h) when shift_row < 0.  h fp32 [M][D], y compute dtype.
 template <typename T>
-hipError_t launch_layernorm(const float* h, T* y, int M, int D, const float* mod, int shift_row,
+hipError_t launch_layernorm(const float* h, T* y, int ldy, int M, int D, const float* mod, int shift_row,
                             int scale_row, int L, hipStream_t s);
 
 // m[task] = e[e_row[task]] + tmod  ([6][D] fp32 each) and the per-task RoPE

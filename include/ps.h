@@ -119,7 +119,7 @@ ps_status ps_context_fetch(const ps_kv_pool* pool, int32_t stream, int32_t block
  * timestep t uses m = e(t) + T_b with rows
  * (shift1, scale1, gate1, shift2, scale2, gate2).
  * block_index selects the block's region of the pool.
- * Requirements: hidden and ffn multiples of 32 (bf16) or 16 (fp32). */
+ * Requirements: hidden and ffn multiples of 64 (bf16) or 32 (fp32). */
 typedef struct {
   int32_t hidden, n_heads, head_dim, ffn;
   int32_t block_index;
