@@ -230,7 +230,8 @@ extern "C" ps_status ps_kv_pool_create(const ps_pool_desc* desc, ps_kv_pool** ou
   if (d.frames <= 0 || d.rows <= 0 || d.cols <= 0)
     return fail(PS_ERR_INVALID_ARG, "pool: token grid must be positive");
   const long long L = (long long)d.frames * d.rows * d.cols;
-  if (L % 8 != 0 || L > (1 << 20)) return fail(PS_ERR_INVALID_ARG, "pool: tokens per chunk (%lld) must be a multiple of 8", L);
+  if (L % 8 != 0 || L < 64 || L > (1 << 20))
+    return fail(PS_ERR_INVALID_ARG, "pool: tokens per chunk (%lld) must be a multiple of 8, at least 64", L);
   if (d.head_dim != 64 && d.head_dim != 128) return fail(PS_ERR_INVALID_ARG, "pool: head_dim must be 64 or 128");
   if (d.n_heads <= 0 || d.n_heads * d.head_dim > 8192) return fail(PS_ERR_INVALID_ARG, "pool: bad n_heads");
   if (d.max_ctx <= 0 || d.max_ctx % 8 != 0) return fail(PS_ERR_INVALID_ARG, "pool: max_ctx must be a positive multiple of 8");

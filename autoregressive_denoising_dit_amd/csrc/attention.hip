@@ -78,30 +78,17 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   const DevTask& tk = tasks[task];
   const int L = pg.L, D = pg.H * HD;
 
-  // key segments: self = read slots then the write slot; cross = the context
-  int n_seg, seg_valid, seg_stride;
-  if (cross) {
-    n_seg = 1; seg_valid = tk.ctx_len; seg_stride = pg.max_ctx;
-  } else {
-    n_seg = tk.n_seg; seg_valid = L; seg_stride = L;
-  }
-  const int n_keys = n_seg * seg_valid;
-  const T* seg_ptr[PS_MAX_WINDOW + 1];
-  if (cross) {
-    seg_ptr[0] = static_cast<const T*>(pg.ctx) + (size_t)tk.ctx_region * pg.ctx_elems;
-  } else {
-#pragma unroll
-    for (int i = 0; i < PS_MAX_WINDOW + 1; ++i)
-      seg_ptr[i] = static_cast<const T*>(pg.kv) +
-                   ((size_t)tk.region * pg.n_slots + tk.slots[i < n_seg ? i : 0]) * pg.slot_elems;
-  }
-  auto locate = [&](int j, int& sgi, int& tok) {
-    if (cross) {
-      sgi = 0; tok = j;
-    } else {
-      sgi = (int)pg.div_L.div((uint32_t)j);
-      tok = j - sgi * L;
-    }
+  // Key segments: self = read slots (oldest first) then the write slot, each
+  // L tokens (L >= the 64-key tile, so a tile spans at most two segments);
+  // cross = the stream's context entry.  The fetch position (segment, offset)
+  // advances tile by tile in scalar registers.
+  const int n_seg = cross ? 1 : tk.n_seg;
+  const int seg_len = cross ? (1 << 30) : L;
+  const int seg_stride = cross ? pg.max_ctx : L;
+  const int n_keys = cross ? tk.ctx_len : n_seg * L;
+  auto seg_base = [&](int i) -> const T* {
+    if (cross) return static_cast<const T*>(pg.ctx) + (size_t)tk.ctx_region * pg.ctx_elems;
+    return static_cast<const T*>(pg.kv) + ((size_t)tk.region * pg.n_slots + tk.slots[i]) * pg.slot_elems;
   };
   const size_t k_off = (size_t)h * seg_stride * HD;
   const size_t v_off = (size_t)pg.H * seg_stride * HD + (size_t)h * HD * seg_stride;
@@ -115,25 +102,34 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   for (int u = 0; u < NU_QK; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + (2 * u + g) * VEC);
 
   u32x4 kr[KLD], vr[VLD];
+  int f_seg = 0, f_off = 0;   // segment and offset of the next tile to fetch
   auto fetch = [&](int tile) {
+    const int t0 = tile * KT;
+    const T* b0 = seg_base(f_seg);
+    const T* b1 = seg_base(min(f_seg + 1, n_seg - 1));
+    const int split = seg_len - f_off;   // tile-relative key where the next segment starts
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
       const int e = tid + NT * i;
       const int row = e / KCH, c = e % KCH;
-      const int key = kBf16 ? perm16(row) : row;
-      const int j = min(tile * KT + key, n_keys - 1);
-      int sgi, tok;
-      locate(j, sgi, tok);
-      kr[i] = *reinterpret_cast<const u32x4*>(seg_ptr[sgi] + k_off + (size_t)tok * HD + c * VEC);
+      const int rel = min(kBf16 ? perm16(row) : row, n_keys - 1 - t0);
+      const bool nx = rel >= split;
+      const int tok = f_off + rel - (nx ? seg_len : 0);
+      kr[i] = *reinterpret_cast<const u32x4*>((nx ? b1 : b0) + k_off + (size_t)tok * HD + c * VEC);
     }
 #pragma unroll
     for (int i = 0; i < VLD; ++i) {
       const int e = tid + NT * i;
       const int f = e / VCH, c = e % VCH;
-      const int j0 = min(tile * KT + c * VEC, n_keys - VEC);
-      int sgi, tok;
-      locate(j0, sgi, tok);
-      vr[i] = *reinterpret_cast<const u32x4*>(seg_ptr[sgi] + v_off + (size_t)f * seg_stride + tok);
+      const int rel = min(c * VEC, n_keys - VEC - t0);
+      const bool nx = rel >= split;
+      const int tok = f_off + rel - (nx ? seg_len : 0);
+      vr[i] = *reinterpret_cast<const u32x4*>((nx ? b1 : b0) + v_off + (size_t)f * seg_stride + tok);
+    }
+    f_off += KT;
+    if (f_off >= seg_len) {
+      f_off -= seg_len;
+      ++f_seg;
     }
   };
   auto stash = [&](int buf) {
@@ -199,7 +195,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
     const bool need = (tile == 0) || (mt > kLazy);
     if (__any(need)) {
       const float shift = need ? mt : 0.0f;
-      const float alpha = exp2f(-shift);
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
       m_run += shift;
 #pragma unroll
       for (int r = 0; r < 16; ++r) negm[r] = -m_run;
@@ -216,7 +212,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = exp2f(s[t][r]);
+      for (int r = 0; r < 16; ++r) s[t][r] = __builtin_amdgcn_exp2f(s[t][r]);
 
     // O^T += V^T P^T
 #pragma unroll

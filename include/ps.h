@@ -73,7 +73,8 @@ typedef struct ps_time_embed ps_time_embed;
  *
  * Token grid: a chunk has L = frames * rows * cols tokens, row-major
  * (token n = (f * rows + y) * cols + x); its frame coordinate for RoPE is
- * chunk * frames + f.  L must be a multiple of 8 and n_ctx a multiple of 8.
+ * chunk * frames + f.  L must be a multiple of 8 and at least 64; n_ctx a
+ * multiple of 8.
  * head_dim must be 64 or 128.  check_slots = 1 turns on the slot ledger:
  * each slot remembers which chunk wrote it, and ps_stage_batch rejects a task
  * whose read slots do not hold chunks c - n_read .. c - 1

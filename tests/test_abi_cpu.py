@@ -66,6 +66,7 @@ def test_validation_fails_before_device_work():
     bad_pools = [
         _lib.PoolDesc(0, 1, 1, 1, 1, 8, 8, 2, 64, 16, 0, 0),      # no streams
         _lib.PoolDesc(1, 1, 1, 1, 1, 3, 5, 2, 64, 16, 0, 0),      # 15 tokens: not a multiple of 8
+        _lib.PoolDesc(1, 1, 1, 1, 1, 4, 8, 2, 64, 16, 0, 0),      # 32 tokens: below one key tile
         _lib.PoolDesc(1, 1, 1, 1, 1, 8, 8, 2, 96, 16, 0, 0),      # head_dim 96
         _lib.PoolDesc(1, 1, 1, 1, 1, 8, 8, 2, 64, 12, 0, 0),      # max_ctx not a multiple of 8
         _lib.PoolDesc(1, 1, 1, 1, 1, 8, 8, 2, 64, 16, 7, 0),      # dtype
