@@ -31,7 +31,7 @@ namespace ps {
 
 namespace {
 
-constexpr int NT = 256, QT = 128, KT = 64;
+constexpr int NT = 512, QT = 256, KT = 64;
 // Lazy rescaling: the running max m used in exp2(s - m) is raised only when a
 // tile's logits exceed it by more than this (log2 units), so probabilities stay
 // <= 2^8 and the O / l rescale is skipped on most tiles.  O / l is unchanged.
@@ -93,7 +93,9 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   const size_t k_off = (size_t)h * seg_stride * HD;
   const size_t v_off = (size_t)pg.H * seg_stride * HD + (size_t)h * HD * seg_stride;
 
-  // this lane's query and its Q fragments (B operand of S^T = K Q^T)
+  // this lane's query and its Q fragments (B operand of S^T = K Q^T); a wave
+  // whose 32 queries all lie past the chunk only helps load key tiles
+  const bool wave_active = qt * QT + wave * 32 < L;
   const int qi = qt * QT + wave * 32 + l32;
   const int qc = min(qi, L - 1);
   const T* qrow = q + ((size_t)task * L + qc) * D + (size_t)h * HD;
@@ -165,6 +167,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
     const int buf = tile & 1;
     if (tile + 1 < n_tiles) fetch(tile + 1);
 
+    if (wave_active) {
     // S^T - m for the 64 keys of this tile (the accumulators start at -m)
     f32x16 s[2];
 #pragma unroll
@@ -246,6 +249,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
       }
     }
 
+    }
     if (tile + 1 < n_tiles) stash(buf ^ 1);
     __syncthreads();
   }
