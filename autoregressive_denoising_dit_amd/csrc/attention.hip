@@ -62,13 +62,17 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   constexpr int VCH = KT / VEC;     // 16-byte chunks per V^T row
   constexpr int NU_QK = KCH / 2;    // k-units of the QK contraction
   constexpr int NU_PV = VCH / 2;    // k-units of the PV contraction
-  constexpr int KLD = KT * KCH / NT;   // K chunks per thread per tile
-  constexpr int VLD = HD * VCH / NT;   // V chunks per thread per tile
   constexpr bool kBf16 = sizeof(T) == 2;
-  __shared__ u32x4 ks[2][KT * KCH];
-  __shared__ u32x4 vs[2][HD * VCH];
+  // LDS ring of NSTG key/value tiles; each tile = K [KT][KCH] then V^T [HD][VCH]
+  constexpr int TILE_CH = KT * KCH + HD * VCH;
+  constexpr int KB = KT * KCH / 64, VB = HD * VCH / 64;   // 1 KB copy blocks per tile
+  constexpr int DPW = (KB + VB) / (NT / 64);              // copies per wave per tile
+  constexpr int NSTG = TILE_CH * 16 * 4 <= 128 * 1024 ? 4 : 2;   // ring depth that fits LDS
+  static_assert((KB + VB) % (NT / 64) == 0, "copy blocks must split evenly over waves");
+  __shared__ u32x4 smem[NSTG * TILE_CH];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int total = n_qt * pg.H * n_tasks;
   const int pid = xcd_remap(blockIdx.x, total);   // a (task, head)'s query tiles share an XCD
@@ -102,50 +106,52 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   u32x4 qf[NU_QK];
 #pragma unroll
   for (int u = 0; u < NU_QK; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + (2 * u + g) * VEC);
+  // take the Q loads' wait here, before the key/value copies are in flight:
+  // a wait inside the tile loop would also wait for those copies
+#pragma unroll
+  for (int u = 0; u < NU_QK; ++u) asm volatile("" : "+v"(qf[u]));
 
-  u32x4 kr[KLD], vr[VLD];
-  int f_seg = 0, f_off = 0;   // segment and offset of the next tile to fetch
-  auto fetch = [&](int tile) {
+  // Key/value tiles are copied from the pool straight into LDS: each copy
+  // instruction moves one 1 KB block (64 lanes x 16 bytes); a lane fetches the
+  // chunk that lands swizzled at its position.  Wave w issues blocks
+  // w * DPW .. w * DPW + DPW - 1 of the tile's [K blocks | V blocks].
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  int f_seg = 0, f_off = 0;   // segment and offset of the next tile to copy
+  auto copy_tile = [&](int tile) {
     const int t0 = tile * KT;
     const T* b0 = seg_base(f_seg);
     const T* b1 = seg_base(min(f_seg + 1, n_seg - 1));
     const int split = seg_len - f_off;   // tile-relative key where the next segment starts
+    const uint32_t stage = lds0 + (uint32_t)((tile % NSTG) * TILE_CH * 16);
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int e = tid + NT * i;
-      const int row = e / KCH, c = e % KCH;
-      const int rel = min(kBf16 ? perm16(row) : row, n_keys - 1 - t0);
-      const bool nx = rel >= split;
-      const int tok = f_off + rel - (nx ? seg_len : 0);
-      kr[i] = *reinterpret_cast<const u32x4*>((nx ? b1 : b0) + k_off + (size_t)tok * HD + c * VEC);
-    }
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int e = tid + NT * i;
-      const int f = e / VCH, c = e % VCH;
-      const int rel = min(c * VEC, n_keys - VEC - t0);
-      const bool nx = rel >= split;
-      const int tok = f_off + rel - (nx ? seg_len : 0);
-      vr[i] = *reinterpret_cast<const u32x4*>((nx ? b1 : b0) + v_off + (size_t)f * seg_stride + tok);
+    for (int i = 0; i < DPW; ++i) {
+      const int bi = wave * DPW + i;   // wave-uniform
+      const T* src;
+      uint32_t dst;
+      if (bi < KB) {
+        const int row = bi * (64 / KCH) + lane / KCH;
+        const int c = (lane % KCH) ^ lds_swz<KCH>(row);
+        const int rel = min(kBf16 ? perm16(row) : row, n_keys - 1 - t0);
+        const bool nx = rel >= split;
+        const int tok = f_off + rel - (nx ? seg_len : 0);
+        src = (nx ? b1 : b0) + k_off + (size_t)tok * HD + c * VEC;
+        dst = stage + bi * 1024;
+      } else {
+        const int vb = bi - KB;
+        const int f = vb * (64 / VCH) + lane / VCH;
+        const int c = (lane % VCH) ^ lds_swz<VCH>(f);
+        const int rel = min(c * VEC, n_keys - VEC - t0);
+        const bool nx = rel >= split;
+        const int tok = f_off + rel - (nx ? seg_len : 0);
+        src = (nx ? b1 : b0) + v_off + (size_t)f * seg_stride + tok;
+        dst = stage + KT * KCH * 16 + vb * 1024;
+      }
+      lds_dma16_global(src, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
     }
     f_off += KT;
     if (f_off >= seg_len) {
       f_off -= seg_len;
       ++f_seg;
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int e = tid + NT * i;
-      const int row = e / KCH, c = e % KCH;
-      ks[buf][row * KCH + (c ^ lds_swz<KCH>(row))] = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int e = tid + NT * i;
-      const int f = e / VCH, c = e % VCH;
-      vs[buf][f * VCH + (c ^ lds_swz<VCH>(f))] = vr[i];
     }
   };
 
@@ -160,12 +166,15 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   for (int r = 0; r < 16; ++r) negm[r] = 0.0f;
 
   const int n_tiles = (n_keys + KT - 1) / KT;
-  fetch(0);
-  stash(0);
-  __syncthreads();
+  for (int t = 0; t < NSTG - 1 && t < n_tiles; ++t) copy_tile(t);
   for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) fetch(tile + 1);
+    // tile lands (copies of later tiles may stay in flight); the barrier also
+    // tells every wave that all reads of the stage about to be refilled are done
+    vm_wait_n((min(tile + NSTG - 2, n_tiles - 1) - tile) * DPW);
+    __syncthreads();
+    if (tile + NSTG - 1 < n_tiles) copy_tile(tile + NSTG - 1);
+    const u32x4* ks = smem + (tile % NSTG) * TILE_CH;
+    const u32x4* vs = ks + KT * KCH;
 
     if (wave_active) {
     // S^T - m for the 64 keys of this tile (the accumulators start at -m)
@@ -175,7 +184,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
       s[t] = negm;
 #pragma unroll
       for (int u = 0; u < NU_QK; ++u) {
-        const u32x4 kf = ks[buf][(t * 32 + l32) * KCH + ((2 * u + g) ^ lds_swz<KCH>(l32))];
+        const u32x4 kf = ks[(t * 32 + l32) * KCH + ((2 * u + g) ^ lds_swz<KCH>(l32))];
         Mfma<T>::unit(s[t], kf, qf[u]);
       }
     }
@@ -244,14 +253,12 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
 #pragma unroll
       for (int i = 0; i < HD / 32; ++i) {
         const int f = i * 32 + l32;
-        const u32x4 vf = vs[buf][f * VCH + ((2 * u + g) ^ lds_swz<VCH>(f))];
+        const u32x4 vf = vs[f * VCH + ((2 * u + g) ^ lds_swz<VCH>(f))];
         Mfma<T>::unit(o[i], vf, pf);
       }
     }
 
     }
-    if (tile + 1 < n_tiles) stash(buf ^ 1);
-    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);

@@ -68,6 +68,26 @@ __device__ __forceinline__ int lds_swz(int row) {
   }
 }
 
+// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 *
+// lane (global_load_lds_dwordx4).  Inline assembly so that the compiler does
+// not make every later LDS read wait for all copies in flight; callers order
+// the copies with vm_wait_n and barriers.
+__device__ __forceinline__ void lds_dma16_global(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_addr), "v"(src) : "memory");
+}
+
+// s_waitcnt vmcnt(n): at most n memory operations of this wave still in flight.
+__device__ __forceinline__ void vm_wait_n(int n) {
+  if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T from_f32(float x);
 template <>
