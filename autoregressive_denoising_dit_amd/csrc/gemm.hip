@@ -9,16 +9,18 @@
 //
 // Tiling: 256 x 256 macro tile, 4 waves in a 2 x 2 grid, each owning a
 // 128 x 128 sub-tile = 4 x 4 MFMA 32x32 accumulators (in AGPRs).  K advances
-// in stages of 64 bytes per row (32 bf16 / 16 fp32) through a ring of 4 LDS
-// stages; operand chunks are XOR-swizzled so that fragment reads of
-// consecutive rows hit distinct banks.  Stage kt is multiplied while the
-// first fragments of stage kt + 1 are read, stage kt + 2 is written to LDS
-// and stage kt + 4 is fetched into registers.
+// in stages of 128 bytes per row (64 bf16 / 32 fp32 = four MFMA k-units)
+// through two LDS stages filled by memory-to-LDS copies.  Operand chunks are
+// XOR-swizzled so that fragment reads of consecutive rows hit distinct banks.
 //
-// Tile order: the linear workgroup id is first remapped so that consecutive
-// ids land on the same XCD (the dispatcher deals workgroups to the 8 XCDs
-// round-robin, each XCD has its own L2), then walked in groups of 8 tile rows
-// so that the tiles an XCD runs together share operand panels in its L2.
+// The copies of a stage are spread over the k-loop, a few between every four
+// MFMAs, instead of issued in one burst per stage: a burst of copies from all
+// waves stalls instruction issue while the memory pipeline drains it, and with
+// one wave per SIMD nothing else keeps the matrix cores busy meanwhile.
+//
+// Tile order: workgroups walk the tile grid in groups of two tile rows, in
+// dispatch order (the dispatcher deals consecutive workgroups to the 8 XCDs
+// round-robin, so each XCD sees a spread of tiles).
 #include <type_traits>
 
 #include "common.h"
@@ -31,6 +33,10 @@ namespace {
 constexpr int BM = 256, BN = 256, ROWB = 128, NT = 256;
 constexpr int CPR = ROWB / 16;  // 16-byte chunks per LDS row (8)
 constexpr int NSTAGE = 2;       // LDS stages of operands
+constexpr int U = ROWB / 32;    // MFMA k-units per stage (4)
+constexpr int RPI = 64 / CPR;   // rows per copy instruction (8)
+constexpr int IPW = (BM / 4) / RPI;   // copy instructions per wave per operand per stage (8)
+constexpr int CPG = IPW / 4;    // copies per group of four MFMAs (2)
 constexpr int EPITCH = 65;      // fp32 row pitch of the epilogue staging (64 columns + 1)
 constexpr int STAGE_CH = (BM + BN) * CPR;               // 16-byte chunks per stage
 constexpr int OPER_BYTES = NSTAGE * STAGE_CH * 16;      // 2 x 64 KB
@@ -48,22 +54,6 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t so
                :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
-// s_waitcnt vmcnt(n) for n in {0, 8, 16} (memory operations still in flight).
-__device__ __forceinline__ void vm_wait(int n) {
-  if (n >= 16) {
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  } else if (n >= 8) {
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-}
-
-__device__ __forceinline__ int xcd_remap(int id, int total) {
-  const int full = (total / 8) * 8;
-  if (id >= full) return id;
-  return (id % 8) * (total / 8) + id / 8;
-}
 
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float k0 = 0.7978845608028654f;  // sqrt(2 / pi)
@@ -241,9 +231,8 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const int l32 = lane & 31, g = lane >> 5;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int total = tiles_m * tiles_n;
-  const int pid = xcd_remap(blockIdx.x, total);
-  constexpr int GROUP = 8;
+  constexpr int GROUP = 2;
+  const int pid = blockIdx.x;
   const int per_group = GROUP * tiles_n;
   const int first_m = (pid / per_group) * GROUP;
   const int gsz = min(tiles_m - first_m, GROUP);
@@ -265,23 +254,22 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const i32x4 rsb = {(int)(uint32_t)b_base, (int)(uint32_t)(b_base >> 32), (int)((size_t)N * K * sizeof(T)),
                      0x00020000};
   const uint32_t a_row = (uint32_t)lda * sizeof(T), b_row = (uint32_t)K * sizeof(T);
-  uint32_t voa[8], vob[8];
+  uint32_t voa[IPW], vob[IPW];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = (wave * 8 + i) * 8 + (lane >> 3);
-    const int cl = (lane & 7) ^ lds_swz<CPR>(row);
+  for (int i = 0; i < IPW; ++i) {
+    const int row = (wave * IPW + i) * RPI + lane / CPR;
+    const int cl = (lane % CPR) ^ lds_swz<CPR>(row);
     voa[i] = (uint32_t)(m0 + row) * a_row + cl * 16;
     vob[i] = (uint32_t)(n0 + row) * b_row + cl * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const uint32_t wblk = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 8 * 1024);
-  auto dma_stage = [&](int kt) {
+  const uint32_t wblk = (uint32_t)__builtin_amdgcn_readfirstlane(wave * IPW * 1024);
+  // copy instruction c of stage kt: c < IPW are A blocks, the rest B blocks
+  auto dma_one = [&](int kt, int c) __attribute__((always_inline)) {
     const uint32_t dst = lds0 + (kt & (NSTAGE - 1)) * (STAGE_CH * 16) + wblk;
     const uint32_t koff = (uint32_t)kt * ROWB;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lds_dma16(rsa, voa[i], koff, dst + i * 1024);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lds_dma16(rsb, vob[i], koff, dst + BM * ROWB + i * 1024);
+    if (c < IPW) lds_dma16(rsa, voa[c], koff, dst + c * 1024);
+    else lds_dma16(rsb, vob[c - IPW], koff, dst + BM * ROWB + (c - IPW) * 1024);
   };
 
   f32x16 acc[4][4];
@@ -295,64 +283,77 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const int wm = wave >> 1, wn = wave & 1;
   const int fsw = lds_swz<CPR>(l32);
   u32x4 fr[2][8];   // MFMA fragments of two k-units (A 0..3, B 4..7)
-  auto frags = [&](int set, int buf, int u) {
-    const u32x4* st = smem + buf * STAGE_CH;
-    const int ch = (2 * u + g) ^ fsw;
+  // One k-unit: 16 MFMAs on fragment set ms in four groups of four.  Each
+  // group also reads two fragments of the next k-unit (set fs, LDS buffer
+  // fbuf, unit fu: the four B fragments first, as every group of the next
+  // unit needs them, then A in order) and issues CPG copy instructions of
+  // operand half dh of stage dkt (none when dkt < 0).
+  auto unit = [&](int ms, int fs, int fbuf, int fu, bool rd, int dkt, int dh) __attribute__((always_inline)) {
+    const u32x4* st = smem + fbuf * STAGE_CH;
+    const int ch = (2 * fu + g) ^ fsw;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fr[set][i] = st[(wm * 128 + i * 32 + l32) * CPR + ch];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fr[set][4 + j] = st[(BM + wn * 128 + j * 32 + l32) * CPR + ch];
-  };
-  auto mma = [&](int set) {
+      for (int j = 0; j < 4; ++j) Mfma<T>::unit(acc[i][j], fr[ms][i], fr[ms][4 + j]);
+      if (rd) {
+        if (i < 2) {
+          fr[fs][4 + 2 * i] = st[(BM + wn * 128 + (2 * i) * 32 + l32) * CPR + ch];
+          fr[fs][5 + 2 * i] = st[(BM + wn * 128 + (2 * i + 1) * 32 + l32) * CPR + ch];
+        } else {
+          fr[fs][2 * (i - 2)] = st[(wm * 128 + (2 * (i - 2)) * 32 + l32) * CPR + ch];
+          fr[fs][2 * (i - 2) + 1] = st[(wm * 128 + (2 * (i - 2) + 1) * 32 + l32) * CPR + ch];
+        }
+      }
+      if (dkt >= 0)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Mfma<T>::unit(acc[i][j], fr[set][i], fr[set][4 + j]);
-  };
-  // Instruction order: LDS fragment reads and the memory-to-LDS copies spread
-  // between the MFMAs so that their latencies hide behind matrix work.
-  auto interleave = [&]() {
-    for (int i = 0; i < 8; ++i) {
+        for (int c = 0; c < CPG; ++c) dma_one(dkt, dh * IPW + i * CPG + c);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Pipeline over stages of 128 bytes of K (four MFMA k-units), two LDS
-  // buffers.  Stage kt + 1 is copied in while stage kt is multiplied; the
-  // barrier sits before the last k-unit of stage kt, so that the first
-  // fragments of stage kt + 1 are read while that unit's MFMAs run, and the
-  // copy of stage kt + 2 (into the buffer just finished) starts right after it.
-  const int nk = K / BK;
-  dma_stage(0);
-  if (nk > 1) {
-    dma_stage(1);
-    vm_wait(16);
-  } else {
-    vm_wait(0);
-  }
-  __syncthreads();
-  frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // Pipeline over stages of 128 bytes of K, two LDS buffers.  The barrier of
+  // stage kt sits before its last k-unit: by then every wave holds all of
+  // stage kt's fragments in registers, so its buffer is refilled with stage
+  // kt + 2 -- the A half of the copies during that last k-unit, the B half
+  // during the first k-unit of stage kt + 1 -- while the first fragments of
+  // stage kt + 1 are read.  Stage kt + 1 must have landed at the barrier.
+  auto stage = [&](int kt, bool copy_b, bool copy_a, bool last) __attribute__((always_inline)) {
     const int buf = kt & 1;
-    frags(1, buf, 1);
-    mma(0);
-    interleave();
-    frags(0, buf, 2);
-    mma(1);
-    interleave();
-    frags(1, buf, 3);
-    mma(0);
-    interleave();
-    if (kt + 1 < nk) {
-      vm_wait(0);
-      __syncthreads();
-      if (kt + 2 < nk) dma_stage(kt + 2);
-      frags(0, buf ^ 1, 0);
+    if (last) {
+#pragma unroll
+      for (int u = 0; u + 1 < U; ++u) unit(u & 1, (u + 1) & 1, buf, u + 1, true, -1, 0);
+      unit((U - 1) & 1, 0, 0, 0, false, -1, 0);
+      return;
     }
-    mma(1);
-    interleave();
+    unit(0, 1, buf, 1, true, copy_b ? kt + 1 : -1, 1);
+#pragma unroll
+    for (int u = 1; u + 1 < U; ++u) unit(u & 1, (u + 1) & 1, buf, u + 1, true, -1, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    unit((U - 1) & 1, U & 1, buf ^ 1, 0, true, copy_a ? kt + 2 : -1, 0);
+  };
+
+  const int nk = K / BK;
+  for (int st = 0; st < NSTAGE && st < nk; ++st)
+#pragma unroll
+    for (int c = 0; c < 2 * IPW; ++c) dma_one(st, c);
+  if (nk > 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // stage 0 landed, stage 1 may fly
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fr[0][i] = smem[((i < 4 ? wm * 128 + i * 32 : BM + wn * 128 + (i - 4) * 32) + l32) * CPR + (g ^ fsw)];
+  int kt = 0;
+  if (nk > 1) {
+    stage(0, false, nk > 2, false);
+    for (kt = 1; kt + 2 < nk; ++kt) stage(kt, true, true, false);   // steady state
+    for (; kt + 1 < nk; ++kt) stage(kt, true, false, false);
   }
+  stage(kt, false, false, true);
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
