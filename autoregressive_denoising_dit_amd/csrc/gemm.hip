@@ -37,11 +37,12 @@ constexpr int U = ROWB / 32;    // MFMA k-units per stage (4)
 constexpr int RPI = 64 / CPR;   // rows per copy instruction (8)
 constexpr int IPW = (BM / 4) / RPI;   // copy instructions per wave per operand per stage (8)
 constexpr int CPG = IPW / 4;    // copies per group of four MFMAs (2)
-constexpr int EPITCH = 65;      // fp32 row pitch of the epilogue staging (64 columns + 1)
+constexpr int EP = 68;          // fp32 row pitch of the epilogue staging (64 columns, 16-byte rows)
 constexpr int STAGE_CH = (BM + BN) * CPR;               // 16-byte chunks per stage
 constexpr int OPER_BYTES = NSTAGE * STAGE_CH * 16;      // 2 x 64 KB
-constexpr int STAGE_BYTES = 4 * 128 * EPITCH * 4;      // 4 waves x 128 rows x pitch
+constexpr int STAGE_BYTES = 4 * 128 * EP * 4;          // 4 waves x 128 rows x pitch
 constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
+constexpr int TAB_BYTES = 160 * 1024 - SMEM_BYTES;     // LDS side tables of the epilogues
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -55,35 +56,85 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t so
 }
 
 
+// GELU, tanh form: z/2 (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3),
+// evaluated as z / (1 + e^(-2u)) (the same function: 1 + tanh(u) = 2 / (1 + e^(-2u)))
+// with the hardware base-2 exponential and reciprocal; saturates to z or 0
+// through inf instead of overflowing.
 __device__ __forceinline__ float gelu_tanh(float z) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2 / pi)
-  return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));
+  constexpr float c = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float t = __builtin_amdgcn_exp2f(c * z * (1.0f + 0.044715f * z * z));
+  return z * __builtin_amdgcn_rcpf(1.0f + t);
 }
 
-// Epilogue of one wave's 128 x 64 staged block (rows rbase.., columns cbase..).
-// Rows (or columns) are processed EB at a time so that EB independent global
-// loads and stores are in flight per lane instead of one.
-constexpr int EB = 8;
+// ------------------------------------------------------------ epilogues
+// After the k-loop each wave stages its 128 x 128 accumulator block in LDS,
+// 64 columns at a time (row pitch EP floats), and stores it with lanes that
+// own 4 consecutive columns (16 lanes per row, 4 rows per instruction), so
+// that every global access is a 16-byte (fp32) or 8-byte (bf16) vector and
+// rows are contiguous runs.  Per-row side data that would otherwise be
+// fetched from memory row by row -- the pool offset of each task's write slot,
+// the RoPE cos/sin tables, the gate rows of the modulation -- is copied into
+// LDS before the k-loop, so the epilogue waits only on LDS.
 
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4 v) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 w = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(p) = w;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// LDS side tables: bytes [0, 256) the pool offset (elements) of each task's
+// write slot, [256, 512) a TabGeo, [512, TAB_BYTES) the data -- RoPE tables
+// (float2) for the QKV epilogue, gate rows (float) for the residual one.
+struct TabGeo {
+  int t0;                      // first task (row block) the tile touches
+  int off_f, off_y, off_x;     // RoPE tables in float2 units from byte 512
+};
+
+// RoPE (cos, sin) of pair dd / 2 of the head dim at token tok of task ti:
+// the frame axis first (seg_f dims), then rows (seg_h), then columns (seg_w).
+template <typename P>
+__device__ __forceinline__ float2 rope_cs(const P& tb, const PoolGeo& pg, int ti, int fl, int yy, int xx,
+                                          int dd) {
+  if (dd < pg.seg_f) return tb.f[(ti * pg.frames + fl) * (pg.seg_f / 2) + (dd >> 1)];
+  if (dd < pg.seg_f + pg.seg_h) return tb.y[yy * (pg.seg_h / 2) + ((dd - pg.seg_f) >> 1)];
+  return tb.x[xx * (pg.seg_w / 2) + ((dd - pg.seg_f - pg.seg_h) >> 1)];
+}
+struct RopePtrs {
+  const float2* f;   // indexed from the first task of the tile
+  const float2* y;
+  const float2* x;
+};
+
+// One wave's staged 128 x 64 block: rows rbase.., columns cbase.. of C.
 template <typename T, int EPI>
-__device__ __forceinline__ void epilogue_half(const float* stg, int rbase, int cbase, int lane, int M, int N,
-                                              const EpiArgs& ep, const DevTask* __restrict__ tasks) {
-  const int col = cbase + lane;
-  const bool col_ok = col < N;
+__device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int cbase, int lane, int M, int N,
+                                               const EpiArgs& ep, const char* tab, int n0) {
   if (cbase >= N) return;
   const int nrows = min(128, M - rbase);
   if (nrows <= 0) return;
   const PoolGeo& pg = ep.pool;
+  const int rq = lane >> 4, cq = lane & 15;   // row within a step of 4, column quad
+  const int col = cbase + 4 * cq;
+  const bool col_ok = col < N;                // N is a multiple of 4
+  const f32x4 bias = col_ok ? ld4(ep.bias + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
   if constexpr (EPI == EPI_QKV || EPI == EPI_CTX_KV) {
     const int D = pg.H * pg.d;
-    const int part = cbase / D;  // a 64-column block lies inside one of q / k / v
+    const int part = cbase / D;   // a 64-column block lies inside one of q / k / v
     const bool transposed = (EPI == EPI_QKV) ? part == 2 : part == 1;
+    const int64_t* soff = reinterpret_cast<const int64_t*>(tab);
     if (transposed) {
-      // values -> V^T [H][d][tokens]: one lane per row (token), columns in turn
+      // values -> V^T [H][d][tokens]: one lane per row (token), 4 columns at a time
       const int stride = (EPI == EPI_QKV) ? pg.L : pg.max_ctx;
-      for (int half = 0; half < 2; ++half) {
+      const int ncol = min(64, N - cbase);
+      for (int half = 0; half < 2 && half * 64 < nrows; ++half) {
         const int rr = half * 64 + lane;
-        if (half * 64 >= nrows) break;
         const bool row_ok = rr < nrows;
         const int row = rbase + rr;
         T* vt;
@@ -91,130 +142,115 @@ __device__ __forceinline__ void epilogue_half(const float* stg, int rbase, int c
         if constexpr (EPI == EPI_QKV) {
           const int ti = row_ok ? (int)pg.div_L.div(row) : 0;
           tok = row - ti * pg.L;
-          const DevTask& tk = tasks[ti];
-          vt = static_cast<T*>(pg.kv) +
-               ((size_t)tk.region * pg.n_slots + tk.slots[tk.n_seg - 1]) * pg.slot_elems +
-               (size_t)pg.H * pg.L * pg.d;
+          vt = static_cast<T*>(pg.kv) + soff[ti] + (size_t)pg.H * pg.L * pg.d;
         } else {
           tok = row;
           vt = static_cast<T*>(ep.ctx_base) + (size_t)pg.H * pg.max_ctx * pg.d;
         }
-        const int ncol = min(64, N - cbase);
-        for (int c0 = 0; c0 < ncol; c0 += EB) {
-          float val[EB];
+        for (int c0 = 0; c0 < ncol; c0 += 4) {
+          const f32x4 v = ld4(stg + min(rr, 127) * EP + c0) + ld4(ep.bias + cbase + c0);
+          const int cc = cbase + c0 - part * D;
+          const int hh = cc >> ep.d_shift, dd = cc & (pg.d - 1);
+          if (row_ok) {
+            T* dst = vt + ((size_t)hh * pg.d + dd) * stride + tok;
 #pragma unroll
-          for (int k = 0; k < EB; ++k) val[k] = stg[rr * EPITCH + c0 + k] + ep.bias[min(cbase + c0 + k, N - 1)];
-#pragma unroll
-          for (int k = 0; k < EB; ++k) {
-            const int cc = cbase + c0 + k - part * D;
-            const int hh = cc >> ep.d_shift, dd = cc & (pg.d - 1);
-            if (row_ok && c0 + k < ncol) vt[((size_t)hh * pg.d + dd) * stride + tok] = from_f32<T>(val[k]);
+            for (int j = 0; j < 4; ++j) dst[(size_t)j * stride] = from_f32<T>(v[j]);
           }
         }
       }
       return;
     }
-    // q or k (QKV) / k (context): one lane per column, rows in turn
-    const float bias = col_ok ? ep.bias[col] : 0.0f;
+    // q or k (QKV) / k (context): lanes own column quads, rows in steps of 4
     const int cc = col - part * D;
     const int hh = cc >> ep.d_shift, dd = cc & (pg.d - 1);
     if constexpr (EPI == EPI_CTX_KV) {
       T* kb = static_cast<T*>(ep.ctx_base);
-      for (int rr = 0; rr < nrows; ++rr) {
-        const float val = stg[rr * EPITCH + lane] + bias;
-        if (col_ok) kb[((size_t)hh * pg.max_ctx + rbase + rr) * pg.d + dd] = from_f32<T>(val);
+      for (int r = rq; r < nrows; r += 4) {
+        const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
+        if (col_ok) store4(kb + ((size_t)hh * pg.max_ctx + rbase + r) * pg.d + dd, v);
       }
       return;
     } else {
-      const float bias_p = (col ^ 1) < N ? ep.bias[col ^ 1] : 0.0f;
-      const float sgn = (dd & 1) ? 1.0f : -1.0f;
-      int seg, pi;
-      if (dd < pg.seg_f) {
-        seg = 0; pi = dd >> 1;
-      } else if (dd < pg.seg_f + pg.seg_h) {
-        seg = 1; pi = (dd - pg.seg_f) >> 1;
-      } else {
-        seg = 2; pi = (dd - pg.seg_f - pg.seg_h) >> 1;
-      }
-      for (int r0 = 0; r0 < nrows; r0 += EB) {
-        float2 cs[EB];
-        int tis[EB], toks[EB];
-#pragma unroll
-        for (int k = 0; k < EB; ++k) {
-          const int row = rbase + min(r0 + k, nrows - 1);
-          const int ti = (int)pg.div_L.div(row);
-          const int tok = row - ti * pg.L;
-          const int yx = (int)pg.div_cols.div(tok);
-          tis[k] = ti;
-          toks[k] = tok;
-          if (seg == 0) {
-            const int fl = (int)pg.div_plane.div(tok);
-            cs[k] = ep.rope_f[(ti * pg.frames + fl) * (pg.seg_f / 2) + pi];
-          } else if (seg == 1) {
-            const int yy = yx - (int)pg.div_rows.div(yx) * pg.rows;
-            cs[k] = pg.rope_y[yy * (pg.seg_h / 2) + pi];
-          } else {
-            const int xx = tok - yx * pg.cols;
-            cs[k] = pg.rope_x[xx * (pg.seg_w / 2) + pi];
-          }
+      const TabGeo& tg = *reinterpret_cast<const TabGeo*>(tab + 256);
+      RopePtrs lt;
+      const float2* tb2 = reinterpret_cast<const float2*>(tab + 512);
+      lt.f = tb2 + tg.off_f;
+      lt.y = tb2 + tg.off_y;
+      lt.x = tb2 + tg.off_x;
+      RopePtrs gt{ep.rope_f + (size_t)tg.t0 * pg.frames * (pg.seg_f / 2), pg.rope_y, pg.rope_x};
+      const bool in_lds = ep.rope_tab != 0;
+      for (int r = rq; r < nrows; r += 4) {
+        const int row = rbase + r;
+        const int ti = (int)pg.div_L.div(row);
+        const int tok = row - ti * pg.L;
+        const int yx = (int)pg.div_cols.div(tok);
+        const int fl = (int)pg.div_plane.div(tok);
+        const int yy = yx - (int)pg.div_rows.div(yx) * pg.rows;
+        const int xx = tok - yx * pg.cols;
+        float2 c0, c1;
+        if (in_lds) {
+          c0 = rope_cs(lt, pg, ti - tg.t0, fl, yy, xx, dd);
+          c1 = rope_cs(lt, pg, ti - tg.t0, fl, yy, xx, dd + 2);
+        } else {
+          c0 = rope_cs(gt, pg, ti - tg.t0, fl, yy, xx, dd);
+          c1 = rope_cs(gt, pg, ti - tg.t0, fl, yy, xx, dd + 2);
         }
-#pragma unroll
-        for (int k = 0; k < EB; ++k) {
-          const int rr = r0 + k;
-          if (rr >= nrows || !col_ok) continue;
-          const int row = rbase + rr;
-          const float val = stg[rr * EPITCH + lane] + bias;
-          const float partner = stg[rr * EPITCH + (lane ^ 1)] + bias_p;
-          const float o = val * cs[k].x + sgn * partner * cs[k].y;
-          if (part == 0) {
-            static_cast<T*>(ep.out)[(size_t)row * D + cc] = from_f32<T>(o * ep.out_scale);
-          } else {
-            const DevTask& tk = tasks[tis[k]];
-            T* kb = static_cast<T*>(pg.kv) +
-                    ((size_t)tk.region * pg.n_slots + tk.slots[tk.n_seg - 1]) * pg.slot_elems;
-            kb[((size_t)hh * pg.L + toks[k]) * pg.d + dd] = from_f32<T>(o);
-          }
+        const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
+        // rotate the pairs (dd, dd + 1) and (dd + 2, dd + 3)
+        f32x4 o;
+        o[0] = v[0] * c0.x - v[1] * c0.y;
+        o[1] = v[1] * c0.x + v[0] * c0.y;
+        o[2] = v[2] * c1.x - v[3] * c1.y;
+        o[3] = v[3] * c1.x + v[2] * c1.y;
+        if (!col_ok) continue;
+        if (part == 0) {
+          store4(static_cast<T*>(ep.out) + (size_t)row * ep.ldo + cc, o * ep.out_scale);
+        } else {
+          T* kb = static_cast<T*>(pg.kv) + soff[ti];
+          store4(kb + ((size_t)hh * pg.L + tok) * pg.d + dd, o);
         }
       }
       return;
     }
+  } else if constexpr (EPI == EPI_RES) {
+    // h_out = h_in + gate * (acc + bias); the residual rows are loaded EB steps
+    // ahead of their use so that their latency overlaps
+    constexpr int EB = 8;
+    const float* gtab = reinterpret_cast<const float*>(tab + 512);
+    const int t0 = reinterpret_cast<const TabGeo*>(tab + 256)->t0;
+    for (int r0 = 0; r0 < nrows; r0 += 4 * EB) {
+      f32x4 hv[EB];
+#pragma unroll
+      for (int k = 0; k < EB; ++k) {
+        const int r = min(r0 + 4 * k + rq, nrows - 1);
+        hv[k] = col_ok ? ld4(ep.h_in + (size_t)(rbase + r) * N + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int k = 0; k < EB; ++k) {
+        const int r = r0 + 4 * k + rq;
+        if (r >= nrows || !col_ok) continue;
+        const int row = rbase + r;
+        f32x4 gv = {1.0f, 1.0f, 1.0f, 1.0f};
+        if (ep.gate_row >= 0) {
+          const int tl = (int)ep.div_L.div(row) - t0;
+          gv = ld4(gtab + tl * BN + (col - n0));
+        }
+        const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
+        *reinterpret_cast<f32x4*>(ep.h_out + (size_t)row * N + col) = hv[k] + gv * v;
+      }
+    }
   } else {
-    const float bias = col_ok ? ep.bias[col] : 0.0f;
-    for (int r0 = 0; r0 < nrows; r0 += EB) {
-      float val[EB];
-#pragma unroll
-      for (int k = 0; k < EB; ++k) val[k] = stg[min(r0 + k, 127) * EPITCH + lane] + bias;
-      if constexpr (EPI == EPI_RES) {
-        float hv[EB], gv[EB];
-#pragma unroll
-        for (int k = 0; k < EB; ++k) {
-          const int row = rbase + min(r0 + k, nrows - 1);
-          const size_t o = (size_t)row * N + (col_ok ? col : 0);
-          hv[k] = ep.h_in[o];
-          gv[k] = 1.0f;
-          if (ep.gate_row >= 0) {
-            const int ti = (int)ep.div_L.div(row);
-            gv[k] = ep.mod[((size_t)ti * 6 + ep.gate_row) * N + (col_ok ? col : 0)];
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < EB; ++k) {
-          if (r0 + k >= nrows || !col_ok) continue;
-          const size_t o = (size_t)(rbase + r0 + k) * N + col;
-          ep.h_out[o] = hv[k] + gv[k] * val[k];
-        }
+    for (int r = rq; r < nrows; r += 4) {
+      const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
+      if (!col_ok) continue;
+      f32x4 o;
+      if constexpr (EPI == EPI_STORE) {
+        o = v * ep.out_scale;
       } else {
 #pragma unroll
-        for (int k = 0; k < EB; ++k) {
-          if (r0 + k >= nrows || !col_ok) continue;
-          const size_t o = (size_t)(rbase + r0 + k) * ep.ldo + col;
-          if constexpr (EPI == EPI_STORE) {
-            static_cast<T*>(ep.out)[o] = from_f32<T>(val[k] * ep.out_scale);
-          } else {
-            static_cast<T*>(ep.out)[o] = from_f32<T>(gelu_tanh(val[k]));
-          }
-        }
+        for (int j = 0; j < 4; ++j) o[j] = gelu_tanh(v[j]);
       }
+      store4(static_cast<T*>(ep.out) + (size_t)(rbase + r) * ep.ldo + col, o);
     }
   }
 }
@@ -224,7 +260,9 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
                                              int M, int N, int K, int lda, EpiArgs ep,
                                              const DevTask* __restrict__ tasks) {
   constexpr int BK = ROWB / sizeof(T);
-  __shared__ u32x4 smem[SMEM_BYTES / 16];
+  constexpr bool kTab = EPI == EPI_QKV || EPI == EPI_RES;
+  __shared__ u32x4 smem[(SMEM_BYTES + (kTab ? TAB_BYTES : 0)) / 16];
+  char* tab = reinterpret_cast<char*>(smem) + SMEM_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -239,6 +277,47 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const int tm = first_m + (pid % per_group) % gsz;
   const int tn = (pid % per_group) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
+
+  // epilogue side tables (read only after the k-loop's barriers)
+  if constexpr (EPI == EPI_QKV) {
+    const PoolGeo& pg = ep.pool;
+    const int n_tasks = (int)pg.div_L.div(M - 1) + 1;
+    if (tid < n_tasks) {
+      const DevTask& tk = tasks[tid];
+      reinterpret_cast<int64_t*>(tab)[tid] =
+          ((int64_t)tk.region * pg.n_slots + tk.slots[tk.n_seg - 1]) * pg.slot_elems;
+    }
+    const int t0 = (int)pg.div_L.div(m0);
+    const int t1 = (int)pg.div_L.div(min(M, m0 + BM) - 1);
+    const int nf = (t1 - t0 + 1) * pg.frames * (pg.seg_f / 2);
+    const int ny = pg.rows * (pg.seg_h / 2), nx = pg.cols * (pg.seg_w / 2);
+    if (tid == 0) {
+      TabGeo* tg = reinterpret_cast<TabGeo*>(tab + 256);
+      tg->t0 = t0;
+      tg->off_f = 0;
+      tg->off_y = nf;
+      tg->off_x = nf + ny;
+    }
+    if (ep.rope_tab) {
+      float2* d2 = reinterpret_cast<float2*>(tab + 512);
+      const float2* f0 = ep.rope_f + (size_t)t0 * pg.frames * (pg.seg_f / 2);
+      for (int i = tid; i < nf + ny + nx; i += NT)
+        d2[i] = i < nf ? f0[i] : i < nf + ny ? pg.rope_y[i - nf] : pg.rope_x[i - nf - ny];
+    }
+  } else if constexpr (EPI == EPI_RES) {
+    if (ep.gate_row >= 0) {
+      const int t0 = (int)ep.div_L.div(m0);
+      const int t1 = (int)ep.div_L.div(min(M, m0 + BM) - 1);
+      if (tid == 0) reinterpret_cast<TabGeo*>(tab + 256)->t0 = t0;
+      float* gt = reinterpret_cast<float*>(tab + 512);
+      for (int i = tid; i < (t1 - t0 + 1) * (BN / 4); i += NT) {
+        const int t = t0 + i / (BN / 4), c4 = (i % (BN / 4)) * 4;
+        const f32x4 v = n0 + c4 < N ? ld4(ep.mod + ((size_t)t * 6 + ep.gate_row) * N + n0 + c4)
+                                    : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        *reinterpret_cast<f32x4*>(gt + (t - t0) * BN + c4) = v;
+      }
+    }
+  }
 
   // Operands stream from memory straight into LDS (buffer_load ... lds): each
   // instruction moves 64 lanes x 16 bytes into one contiguous 1 KB block =
@@ -357,12 +436,11 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
-  // The accumulators go through LDS, 64 columns at a time (row pitch 65
-  // floats), so that the epilogue walks rows (or columns) with one lane per
-  // element and every global store is a contiguous run.
-  float* stg = reinterpret_cast<float*>(smem) + wave * (128 * EPITCH);
+  float* stg = reinterpret_cast<float*>(smem) + wave * (128 * EP);
 #pragma unroll
   for (int hlf = 0; hlf < 2; ++hlf) {
+    // each wave stages into and reads back its own region only; LDS accesses
+    // of one wave complete in order, so no barrier is needed between halves
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -370,11 +448,9 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-          stg[row * EPITCH + jj * 32 + l32] = acc[i][2 * hlf + jj][r];
+          stg[row * EP + jj * 32 + l32] = acc[i][2 * hlf + jj][r];
         }
-    __syncthreads();
-    epilogue_half<T, EPI>(stg, m0 + wm * 128, n0 + wn * 128 + hlf * 64, lane, M, N, ep, tasks);
-    __syncthreads();
+    epilogue_block<T, EPI>(stg, m0 + wm * 128, n0 + wn * 128 + hlf * 64, lane, M, N, ep, tab, n0);
   }
 }
 
@@ -390,12 +466,27 @@ hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, i
     return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid(tiles), block(NT);
+  // LDS side tables of the epilogue: a tile's rows span at most BM / L + 2 tasks
+  EpiArgs e = ep;
+  if (epi == EPI_QKV || epi == EPI_RES) {
+    const int L = epi == EPI_QKV ? ep.pool.L : ep.L;
+    if (L < 64) return hipErrorInvalidValue;
+    const int span = BM / L + 2;
+    if (epi == EPI_RES && span * BN * 4 > TAB_BYTES - 512) return hipErrorInvalidValue;
+    if (epi == EPI_QKV) {
+      const PoolGeo& pg = ep.pool;
+      const int64_t pairs = (int64_t)span * pg.frames * (pg.seg_f / 2) + (int64_t)pg.rows * (pg.seg_h / 2) +
+                            (int64_t)pg.cols * (pg.seg_w / 2);
+      e.rope_tab = pairs * 8 <= TAB_BYTES - 512 ? 1 : 0;
+      if (M / L > 32) return hipErrorInvalidValue;   // one write-slot offset per task
+    }
+  }
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((k_gemm<T, EPI_QKV>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
-    case EPI_CTX_KV: hipLaunchKernelGGL((k_gemm<T, EPI_CTX_KV>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
-    case EPI_STORE: hipLaunchKernelGGL((k_gemm<T, EPI_STORE>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
-    case EPI_GELU: hipLaunchKernelGGL((k_gemm<T, EPI_GELU>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
-    case EPI_RES: hipLaunchKernelGGL((k_gemm<T, EPI_RES>), grid, block, 0, s, A, B, M, N, K, lda, ep, tt); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm<T, EPI_QKV>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_CTX_KV: hipLaunchKernelGGL((k_gemm<T, EPI_CTX_KV>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_STORE: hipLaunchKernelGGL((k_gemm<T, EPI_STORE>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_GELU: hipLaunchKernelGGL((k_gemm<T, EPI_GELU>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_RES: hipLaunchKernelGGL((k_gemm<T, EPI_RES>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

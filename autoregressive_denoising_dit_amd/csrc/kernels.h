@@ -25,6 +25,7 @@ struct EpiArgs {
   int gate_row = -1;
   int L = 1;
   const float2* rope_f = nullptr; // [n_tasks][frames][seg_f / 2]
+  int rope_tab = 0;               // set by the launcher: RoPE tables fit the kernel's LDS
   void* ctx_base = nullptr;
   int d_shift = 0;                // log2(head_dim)
   FastDiv div_L;                  // rows per task
