@@ -5,6 +5,9 @@
 // LayerNorm: one wave per row; the row stays in registers between the mean,
 // the variance and the normalisation, so h is read from HBM once and y
 // written once (16-byte loads where D % 256 == 0).  Statistics in fp32.
+// For the common hidden sizes the row length is a template constant, so that
+// all of a row's loads -- and the task's modulation rows, which are L2
+// resident -- are in flight together before the first use.
 #include <math.h>
 
 #include "common.h"
@@ -98,6 +101,57 @@ __global__ void __launch_bounds__(256) k_layernorm(const float* __restrict__ h, 
         for (int k = 0; k < VW; ++k) w[k] = o[k];
         *reinterpret_cast<vf*>(yr + c0) = w;
       }
+    }
+  }
+}
+
+// Fixed-width variant: NI float4 per lane (D = 256 NI); MOD = modulated.
+template <typename T, int NI, bool MOD>
+__global__ void __launch_bounds__(256) k_layernorm_n(const float* __restrict__ h, T* __restrict__ y, int ldy,
+                                                     int M, const float* __restrict__ mod, int shift_row,
+                                                     int scale_row, FastDiv div_L) {
+  constexpr int D = 256 * NI;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float* hr = h + (size_t)row * D;
+  f32x4 v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) v[i] = *reinterpret_cast<const f32x4*>(hr + (i * 64 + lane) * 4);
+  f32x4 sh[MOD ? NI : 1], sc[MOD ? NI : 1];
+  if constexpr (MOD) {
+    const int ti = (int)div_L.div(row);
+    const float* shift = mod + ((size_t)ti * 6 + shift_row) * D;
+    const float* scale = mod + ((size_t)ti * 6 + scale_row) * D;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      sh[i] = *reinterpret_cast<const f32x4*>(shift + (i * 64 + lane) * 4);
+      sc[i] = *reinterpret_cast<const f32x4*>(scale + (i * 64 + lane) * 4);
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  const float mean = wave_sum(sum) * (1.0f / D);
+  float sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float dlt = v[i][k] - mean;
+      sq += dlt * dlt;
+    }
+  const float rstd = 1.0f / sqrtf(wave_sum(sq) * (1.0f / D) + 1e-6f);
+  T* yr = y + (size_t)row * ldy;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    f32x4 o = (v[i] - mean) * rstd;
+    if constexpr (MOD) o = o * (1.0f + sc[i]) + sh[i];
+    const int c0 = (i * 64 + lane) * 4;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<bf16x4*>(yr + c0) = bf16x4{(bf16)o[0], (bf16)o[1], (bf16)o[2], (bf16)o[3]};
+    } else {
+      *reinterpret_cast<f32x4*>(yr + c0) = o;
     }
   }
 }
@@ -233,6 +287,29 @@ template <typename T>
 hipError_t launch_layernorm(const float* h, T* y, int ldy, int M, int D, const float* mod, int shift_row,
                             int scale_row, int L, hipStream_t s) {
   dim3 grid((M + 3) / 4), block(256);
+  const bool m = shift_row >= 0;
+  const FastDiv dl((uint32_t)L);
+#define PS_LN_CASE(NI)                                                                                  \
+  case NI:                                                                                              \
+    if (m)                                                                                              \
+      hipLaunchKernelGGL((k_layernorm_n<T, NI, true>), grid, block, 0, s, h, y, ldy, M, mod, shift_row,   \
+                         scale_row, dl);                                                                \
+    else                                                                                                \
+      hipLaunchKernelGGL((k_layernorm_n<T, NI, false>), grid, block, 0, s, h, y, ldy, M, mod, shift_row,  \
+                         scale_row, dl);                                                                \
+    return hipGetLastError();
+  if (D % 256 == 0) {
+    switch (D / 256) {
+      PS_LN_CASE(6)
+      PS_LN_CASE(8)
+      PS_LN_CASE(12)
+      PS_LN_CASE(16)
+      PS_LN_CASE(20)
+      PS_LN_CASE(24)
+      default: break;
+    }
+  }
+#undef PS_LN_CASE
   if (D % 256 == 0 && D <= 8192) {
     hipLaunchKernelGGL((k_layernorm<T, 4, 32>), grid, block, 0, s, h, y, ldy, M, D, mod, shift_row, scale_row, L);
   } else if (D % 128 == 0 && D <= 8192) {
