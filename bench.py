@@ -135,6 +135,84 @@ def run_stage_bench(cfg, n_tasks, steps, warmup):
     return sec, trace
 
 
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size: the reference that scales the HBM
+    byte counters (FETCH_SIZE, WRITE_SIZE) of a profiling run to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def _short_kernel(name):
+    for key in ("k_attn", "k_gemm", "k_layernorm_n", "k_layernorm", "k_euler", "k_modulation", "k_put_tasks",
+                "k_entry_load", "k_gemv", "copy"):
+        if key in name:
+            return key
+    return None
+
+
+def pmc_summary(dirs):
+    """Per-dispatch averages of the counters of rocprofv3 --pmc CSV output, per
+    kernel.  Self- and cross-attention share one kernel; in a step the
+    self-attention launch comes first, so attention dispatches alternate."""
+    import csv
+    import glob
+    per = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(path)):
+                k = _short_kernel(row["Kernel_Name"])
+                if k is None:
+                    continue
+                if k == "k_gemm":
+                    # the epilogue is the last template argument: k_gemm<T, E>
+                    k = "k_gemm_E" + row["Kernel_Name"].split("Li", 1)[1][:1] if "Li" in row["Kernel_Name"] else k
+                key = (k, int(row["Dispatch_Id"]))
+                per.setdefault(key, {})
+                c = row["Counter_Name"]
+                per[key][c] = per[key].get(c, 0.0) + float(row["Counter_Value"])
+    out = {}
+    attn = sorted(d for (k, d) in per if k == "k_attn")
+    for (k, did), cs in per.items():
+        name = k
+        if k == "k_attn":
+            name = "attn_self" if attn.index(did) % 2 == 0 else "attn_cross"
+        agg = out.setdefault(name, {"dispatches": 0})
+        agg["dispatches"] += 1
+        for c, v in cs.items():
+            agg[c] = agg.get(c, 0.0) + v
+    for name, agg in out.items():
+        n = agg["dispatches"]
+        for c in list(agg):
+            if c != "dispatches":
+                agg[c] = round(agg[c] / n, 3)
+    print(json.dumps(out, indent=1, sort_keys=True), flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel's source changed since it was taken."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel") != kernel:
+        return None
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel, digest in rec["sources"].items():
+        f = os.path.join(root, rel)
+        if not os.path.exists(f) or hashlib.sha256(open(f, "rb").read()).hexdigest() != digest:
+            return None
+    kib = rec["fetch_kib"] * rec["copy_fetch_scale"] + rec["write_kib"] * rec["copy_write_scale"]
+    return int(round(kib * 1024))
+
+
 def cpu_baseline(cfg, n_read, budget_s=30.0):
     """The float64 CPU oracle on one task of the workload (a bounded sample)."""
     import numpy as np
@@ -178,7 +256,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5", choices=["c2", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="only summarise rocprofv3 --pmc CSV output per kernel and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
@@ -188,6 +273,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     cfg = get(args.workload)
     n_tasks = cfg.batch
     n_read = cfg.window
@@ -211,10 +299,12 @@ def main():
     avg_s = trace[dom][1] / trace[dom][0] * 1e-3
     if kind == "flop":
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(amount / avg_s / 1e12, 2), "peak": peak / 1e12,
-                "unit": "TFLOP/s", "frac": round(amount / avg_s / peak, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(amount / avg_s / peak, 4)}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(amount / avg_s / 1e9, 1), "peak": HBM_PEAK / 1e9,
-                "unit": "GB/s", "frac": round(amount / avg_s / HBM_PEAK, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(amount / avg_s / HBM_PEAK, 4)}
+    # measured HBM bytes per launch of the dominant kernel (profiles/traffic.json)
+    roof["traffic"] = measured_traffic(dom)
     out = {
         "metric": "stage tasks/sec + steady-state chunk interval (ms) on 1 MI355X; % MFMA peak",
         "value": round(n_tasks / sec, 2),
