@@ -17,11 +17,11 @@
 // no LDS round trip for P.  V is stored transposed in the pool (V^T [d][L])
 // so that P V contracts along contiguous memory.
 //
-// Work split: one workgroup = (128-query tile, head, task); 4 waves x 32
-// queries.  Keys stream through LDS in 64-key tiles, double-buffered, with
-// the next tile fetched into registers while the current one is used.
-// Softmax runs in fp32 with exp2 on logits pre-scaled by log2(e)/sqrt(d)
-// (the scale is folded into q by the producing GEMM).
+// Work split: one workgroup = (256-query tile, head, task); 8 waves x 32
+// queries, two waves per SIMD.  Keys stream through LDS in 64-key tiles,
+// copied from the pool straight into LDS (no register staging) through a ring
+// of tiles several deep.  Softmax runs in fp32 with exp2 on logits pre-scaled
+// by log2(e)/sqrt(d) (the scale is folded into q by the producing GEMM).
 #include <math.h>
 
 #include "common.h"
@@ -86,13 +86,17 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   // L tokens (L >= the 64-key tile, so a tile spans at most two segments);
   // cross = the stream's context entry.  The fetch position (segment, offset)
   // advances tile by tile in scalar registers.
-  const int n_seg = cross ? 1 : tk.n_seg;
+  const int n_seg = cross ? 1 : __builtin_amdgcn_readfirstlane(tk.n_seg);
   const int seg_len = cross ? (1 << 30) : L;
   const int seg_stride = cross ? pg.max_ctx : L;
-  const int n_keys = cross ? tk.ctx_len : n_seg * L;
+  const int n_keys = cross ? __builtin_amdgcn_readfirstlane(tk.ctx_len) : n_seg * L;
+  // task fields are read once into registers (the copy instructions clobber
+  // memory as far as the compiler knows, which would force reloads)
+  const T* const region_base = cross ? static_cast<const T*>(pg.ctx) + (size_t)tk.ctx_region * pg.ctx_elems
+                                     : static_cast<const T*>(pg.kv) + (size_t)tk.region * pg.n_slots * pg.slot_elems;
   auto seg_base = [&](int i) -> const T* {
-    if (cross) return static_cast<const T*>(pg.ctx) + (size_t)tk.ctx_region * pg.ctx_elems;
-    return static_cast<const T*>(pg.kv) + ((size_t)tk.region * pg.n_slots + tk.slots[i]) * pg.slot_elems;
+    if (cross) return region_base;
+    return region_base + (size_t)tk.slots[i] * pg.slot_elems;
   };
   const size_t k_off = (size_t)h * seg_stride * HD;
   const size_t v_off = (size_t)pg.H * seg_stride * HD + (size_t)h * HD * seg_stride;
@@ -117,41 +121,75 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   // w * DPW .. w * DPW + DPW - 1 of the tile's [K blocks | V blocks].
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   int f_seg = 0, f_off = 0;   // segment and offset of the next tile to copy
+  // Per-lane byte offsets of this wave's copy blocks inside a tile that lies
+  // in one segment (all but the tiles that straddle a segment boundary and
+  // the ragged last one): the source of such a tile is a scalar base plus
+  // these constants, so a copy costs one 64-bit add instead of the full
+  // per-lane index arithmetic.
+  uint32_t lane_off[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int bi = wave * DPW + i;
+    if (bi < KB) {
+      const int row = bi * (64 / KCH) + lane / KCH;
+      const int c = (lane % KCH) ^ lds_swz<KCH>(row);
+      lane_off[i] = (uint32_t)(((kBf16 ? perm16(row) : row) * HD + c * VEC) * sizeof(T));
+    } else {
+      const int vb = bi - KB;
+      const int f = vb * (64 / VCH) + lane / VCH;
+      const int c = (lane % VCH) ^ lds_swz<VCH>(f);
+      lane_off[i] = (uint32_t)(((size_t)f * seg_stride + c * VEC) * sizeof(T));
+    }
+  }
+  const T* cur_base = seg_base(0);   // base of segment f_seg
   auto copy_tile = [&](int tile) {
     const int t0 = tile * KT;
-    const T* b0 = seg_base(f_seg);
-    const T* b1 = seg_base(min(f_seg + 1, n_seg - 1));
+    const T* b0 = cur_base;
     const int split = seg_len - f_off;   // tile-relative key where the next segment starts
     const uint32_t stage = lds0 + (uint32_t)((tile % NSTG) * TILE_CH * 16);
+    if (split >= KT && t0 + KT <= n_keys) {
+      const char* kb = reinterpret_cast<const char*>(b0 + k_off + (size_t)f_off * HD);
+      const char* vb = reinterpret_cast<const char*>(b0 + v_off + f_off);
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      const int bi = wave * DPW + i;   // wave-uniform
-      const T* src;
-      uint32_t dst;
-      if (bi < KB) {
-        const int row = bi * (64 / KCH) + lane / KCH;
-        const int c = (lane % KCH) ^ lds_swz<KCH>(row);
-        const int rel = min(kBf16 ? perm16(row) : row, n_keys - 1 - t0);
-        const bool nx = rel >= split;
-        const int tok = f_off + rel - (nx ? seg_len : 0);
-        src = (nx ? b1 : b0) + k_off + (size_t)tok * HD + c * VEC;
-        dst = stage + bi * 1024;
-      } else {
-        const int vb = bi - KB;
-        const int f = vb * (64 / VCH) + lane / VCH;
-        const int c = (lane % VCH) ^ lds_swz<VCH>(f);
-        const int rel = min(c * VEC, n_keys - VEC - t0);
-        const bool nx = rel >= split;
-        const int tok = f_off + rel - (nx ? seg_len : 0);
-        src = (nx ? b1 : b0) + v_off + (size_t)f * seg_stride + tok;
-        dst = stage + KT * KCH * 16 + vb * 1024;
+      for (int i = 0; i < DPW; ++i) {
+        const int bi = wave * DPW + i;   // wave-uniform
+        const char* src = (bi < KB ? kb : vb) + lane_off[i];
+        const uint32_t dst = stage + (bi < KB ? bi * 1024 : KT * KCH * 16 + (bi - KB) * 1024);
+        lds_dma16_global(src, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
       }
-      lds_dma16_global(src, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
+    } else {
+      const T* b1 = seg_base(min(f_seg + 1, n_seg - 1));
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int bi = wave * DPW + i;   // wave-uniform
+        const T* src;
+        uint32_t dst;
+        if (bi < KB) {
+          const int row = bi * (64 / KCH) + lane / KCH;
+          const int c = (lane % KCH) ^ lds_swz<KCH>(row);
+          const int rel = min(kBf16 ? perm16(row) : row, n_keys - 1 - t0);
+          const bool nx = rel >= split;
+          const int tok = f_off + rel - (nx ? seg_len : 0);
+          src = (nx ? b1 : b0) + k_off + (size_t)tok * HD + c * VEC;
+          dst = stage + bi * 1024;
+        } else {
+          const int vb = bi - KB;
+          const int f = vb * (64 / VCH) + lane / VCH;
+          const int c = (lane % VCH) ^ lds_swz<VCH>(f);
+          const int rel = min(c * VEC, n_keys - VEC - t0);
+          const bool nx = rel >= split;
+          const int tok = f_off + rel - (nx ? seg_len : 0);
+          src = (nx ? b1 : b0) + v_off + (size_t)f * seg_stride + tok;
+          dst = stage + KT * KCH * 16 + vb * 1024;
+        }
+        lds_dma16_global(src, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
+      }
     }
     f_off += KT;
     if (f_off >= seg_len) {
       f_off -= seg_len;
       ++f_seg;
+      cur_base = seg_base(min(f_seg, n_seg - 1));
     }
   };
 

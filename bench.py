@@ -122,17 +122,34 @@ def run_stage_bench(cfg, n_tasks, steps, warmup):
         step(tau)
     torch.cuda.synchronize()
     _lib.trace_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record()
     for tau in range(steps):
         step(tau)
+        ev[tau + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     trace = _lib.trace_read()
     _lib.trace_enable(False)
     assert torch.isfinite(st["h"]).all().item(), "non-finite stage output"
     sec = (t1 - t0) / steps
-    return sec, trace
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return sec, trace, per_step
+
+
+def shader_clock_mhz():
+    """Current shader clock from the driver's DPM table (best effort; None if unreadable)."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if line.strip().endswith("*"):
+                    return int(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
@@ -252,8 +269,8 @@ def cpu_baseline(cfg, n_read, budget_s=30.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c5", choices=["c2", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -279,7 +296,8 @@ def main():
     cfg = get(args.workload)
     n_tasks = cfg.batch
     n_read = cfg.window
-    sec, trace = run_stage_bench(cfg, n_tasks, args.steps, args.warmup)
+    sec, trace, per_step = run_stage_bench(cfg, n_tasks, args.steps, args.warmup)
+    sclk = shader_clock_mhz()
     flops_step = n_tasks * stage_flops(cfg, n_read)
     peak = PEAK[cfg.dtype]
     work = kernel_work(cfg, n_tasks, n_read)
@@ -325,6 +343,10 @@ def main():
         "chunk_interval_ms": round(sec * 1e3 * cfg.n_steps, 3),
         "mfma_frac": round(flops_step / sec / peak, 4),
         "stage_tflops": round(flops_step / sec / 1e12, 1),
+        # HIP events between consecutive steps of the timed region
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 3), "p10": round(per_step[len(per_step) // 10], 3),
+                    "p90": round(per_step[min(len(per_step) - 1, (9 * len(per_step)) // 10)], 3)},
+        "sclk_mhz_after": sclk,
         "kernels": kernels,
         "roofline": roof,
     }
