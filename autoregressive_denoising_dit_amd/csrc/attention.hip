@@ -148,14 +148,16 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
     const int split = seg_len - f_off;   // tile-relative key where the next segment starts
     const uint32_t stage = lds0 + (uint32_t)((tile % NSTG) * TILE_CH * 16);
     if (split >= KT && t0 + KT <= n_keys) {
-      const char* kb = reinterpret_cast<const char*>(b0 + k_off + (size_t)f_off * HD);
-      const char* vb = reinterpret_cast<const char*>(b0 + v_off + f_off);
+      // buffer resources over this head's K and V^T of the segment; the tile
+      // offset goes in the scalar offset, the lane's in the 32-bit vector one
+      const i32x4 rk = make_rsrc(b0 + k_off, 0xffffffffu), rv = make_rsrc(b0 + v_off, 0xffffffffu);
+      const uint32_t sk = (uint32_t)f_off * HD * sizeof(T), sv = (uint32_t)f_off * sizeof(T);
 #pragma unroll
       for (int i = 0; i < DPW; ++i) {
         const int bi = wave * DPW + i;   // wave-uniform
-        const char* src = (bi < KB ? kb : vb) + lane_off[i];
         const uint32_t dst = stage + (bi < KB ? bi * 1024 : KT * KCH * 16 + (bi - KB) * 1024);
-        lds_dma16_global(src, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
+        if (bi < KB) lds_dma16_buf(rk, lane_off[i], sk, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
+        else lds_dma16_buf(rv, lane_off[i], sv, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
       }
     } else {
       const T* b1 = seg_base(min(f_seg + 1, n_seg - 1));

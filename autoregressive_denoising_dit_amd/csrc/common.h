@@ -77,6 +77,23 @@ __device__ __forceinline__ void lds_dma16_global(const void* src, uint32_t lds_a
                :: "s"(lds_addr), "v"(src) : "memory");
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes) with raw (unstrided) addressing;
+// reads past the end return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)bytes, 0x00020000};
+}
+
+// 16 bytes per lane from rsrc + voff + soff straight into LDS at lds_addr +
+// 16 * lane (buffer_load_dwordx4 ... lds): no per-lane address arithmetic
+// beyond the 32-bit lane offset.
+__device__ __forceinline__ void lds_dma16_buf(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
 // s_waitcnt vmcnt(n): at most n memory operations of this wave still in flight.
 __device__ __forceinline__ void vm_wait_n(int n) {
   if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");

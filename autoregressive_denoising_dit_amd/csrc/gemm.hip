@@ -44,16 +44,6 @@ constexpr int STAGE_BYTES = 4 * 128 * EP * 4;          // 4 waves x 128 rows x p
 constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
 constexpr int TAB_BYTES = 160 * 1024 - SMEM_BYTES;     // LDS side tables of the epilogues
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// 16 bytes per lane from a raw buffer straight into LDS at lds_addr + 16 * lane.
-// Written as inline assembly so that the compiler does not treat every later
-// LDS read as dependent on it (it would wait for all copies in flight); the
-// kernel orders these copies itself with vm_wait + barriers.
-__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
 
 
 // GELU, tanh form: z/2 (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3),
@@ -347,8 +337,8 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   auto dma_one = [&](int kt, int c) __attribute__((always_inline)) {
     const uint32_t dst = lds0 + (kt & (NSTAGE - 1)) * (STAGE_CH * 16) + wblk;
     const uint32_t koff = (uint32_t)kt * ROWB;
-    if (c < IPW) lds_dma16(rsa, voa[c], koff, dst + c * 1024);
-    else lds_dma16(rsb, vob[c - IPW], koff, dst + BM * ROWB + (c - IPW) * 1024);
+    if (c < IPW) lds_dma16_buf(rsa, voa[c], koff, dst + c * 1024);
+    else lds_dma16_buf(rsb, vob[c - IPW], koff, dst + BM * ROWB + (c - IPW) * 1024);
   };
 
   f32x16 acc[4][4];
