@@ -121,6 +121,37 @@ def test_stage_bf16_tiny_shapes():
     _check_case(case)
 
 
+def test_stage_fp32_widest_window():
+    """The widest window the boundary allows (8 prior chunks = 9 key segments),
+    next to a task with none; context of 8 tokens (one 16-byte chunk per key
+    row in fp32), the smallest the pool accepts."""
+    cfg = with_(C1, n_ctx=8)
+    tasks = [(0, 9, 0, 8), (0, 8, 1, 8), (0, 0, 1, 0)]
+    case = StageCase(cfg, tasks, n_slots=10).run_gpu()
+    case.run_oracle()
+    _check_case(case)
+
+
+def test_stage_fp32_largest_batch():
+    """32 tasks (the most one batch takes): 4 streams x 2 steps x 4 chunks, each
+    chunk reading the two before it, one of them written by the same batch.
+    With 64-token chunks a 256-row GEMM tile spans several tasks."""
+    cfg = C1
+    tasks = [(sg, c, s, 2) for sg in range(4) for s in range(2) for c in range(10, 14)]
+    case = StageCase(cfg, tasks, n_slots=8).run_gpu()
+    case.run_oracle(task_ids=[0, 5, 13, 22, 31])
+    _check_case(case, task_ids=[0, 5, 13, 22, 31])
+
+
+def test_stage_bf16_head_dim_64_ragged_context():
+    """bf16 with 64-dim heads at full chunk length (ragged last key tile) and a
+    context of 200 tokens (ragged last cross tile); all rows of both tasks."""
+    cfg = with_(C2, hidden=512, heads=8, head_dim=64, ffn=1024, n_ctx=200)
+    case = StageCase(cfg, [(0, 5, 1, 3), (1, 4, 2, 2)]).run_gpu()
+    case.run_oracle()
+    _check_case(case)
+
+
 def test_stage_c2_single_task_full():
     """Wan2.1-1.3B-shaped stage at batch 1, full window, every output row."""
     cfg = C2
