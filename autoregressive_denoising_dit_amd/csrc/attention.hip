@@ -17,10 +17,11 @@
 // no LDS round trip for P.  V is stored transposed in the pool (V^T [d][L])
 // so that P V contracts along contiguous memory.
 //
-// Work split: one workgroup = (256-query tile, head, task); 8 waves x 32
-// queries, two waves per SIMD.  Keys stream through LDS in 64-key tiles,
-// copied from the pool straight into LDS (no register staging) through a ring
-// of tiles several deep.  Softmax runs in fp32 with exp2 on logits pre-scaled
+// Work split: one workgroup = (query tile, head, task), one wave per 32
+// queries: in bf16 4 waves (128 queries) with a ring of two 64-key tiles, two
+// workgroups per CU; in fp32 8 waves (256 queries) with a deeper ring.  Key /
+// value tiles are copied from the pool straight into LDS (no register
+// staging).  Softmax runs in fp32 with exp2 on logits pre-scaled
 // by log2(e)/sqrt(d) (the scale is folded into q by the producing GEMM).
 #include <math.h>
 
@@ -31,7 +32,7 @@ namespace ps {
 
 namespace {
 
-constexpr int NT = 512, QT = 256, KT = 64;
+constexpr int KT = 64;
 // Lazy rescaling: the running max m used in exp2(s - m) is raised only when a
 // tile's logits exceed it by more than this (log2 units), so probabilities stay
 // <= 2^8 and the O / l rescale is skipped on most tiles.  O / l is unchanged.
@@ -53,7 +54,9 @@ __device__ __forceinline__ int perm16(int r) {
   return (r & ~15) | (qs << 2) | (r & 3);
 }
 
-template <typename T, int HD>
+// NT threads (NT / 64 waves of 32 queries each) per workgroup, a ring of RING
+// key/value tiles (0: the deepest that fits 128 KB of LDS).
+template <typename T, int HD, int NT, int RING>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const DevTask* __restrict__ tasks,
        int cross, int n_qt, int n_tasks) {
@@ -67,7 +70,8 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   constexpr int TILE_CH = KT * KCH + HD * VCH;
   constexpr int KB = KT * KCH / 64, VB = HD * VCH / 64;   // 1 KB copy blocks per tile
   constexpr int DPW = (KB + VB) / (NT / 64);              // copies per wave per tile
-  constexpr int NSTG = TILE_CH * 16 * 4 <= 128 * 1024 ? 4 : 2;   // ring depth that fits LDS
+  constexpr int QT = NT / 2;   // queries per workgroup
+  constexpr int NSTG = RING ? RING : TILE_CH * 16 * 4 <= 128 * 1024 ? 4 : 2;
   static_assert((KB + VB) % (NT / 64) == 0, "copy blocks must split evenly over waves");
   __shared__ u32x4 smem[NSTG * TILE_CH];
 
@@ -327,19 +331,32 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
 
 }  // namespace
 
+template <typename T, int HD>
+hipError_t launch_attention_hd(bool cross, const T* q, T* out, int ldo, const PoolGeo& pg, const DevTask* tt,
+                               int n_tasks, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // 4-wave workgroups with a two-tile ring: two of them share a CU, and as
+    // they run unsynchronised, one's softmax and start-up (query loads, first
+    // tiles) overlap the other's matrix work.  (Measured a little faster than
+    // 8-wave workgroups with a four-tile ring, which load each key/value tile
+    // once per 256 queries instead of 128.)
+    const int n_qt = (pg.L + 127) / 128;
+    hipLaunchKernelGGL((k_attn<T, HD, 256, 2>), dim3(n_qt * pg.H * n_tasks), dim3(256), 0, s, q, out, ldo, pg, tt,
+                       cross ? 1 : 0, n_qt, n_tasks);
+  } else {
+    const int n_qt = (pg.L + 255) / 256;
+    hipLaunchKernelGGL((k_attn<T, HD, 512, 0>), dim3(n_qt * pg.H * n_tasks), dim3(512), 0, s, q, out, ldo, pg, tt,
+                       cross ? 1 : 0, n_qt, n_tasks);
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_attention(bool cross, const T* q, T* out, int ldo, const PoolGeo& pg, const DevTask* tt,
                             int n_tasks, hipStream_t s) {
-  const int n_qt = (pg.L + QT - 1) / QT;
-  dim3 grid(n_qt * pg.H * n_tasks), block(NT);
-  if (pg.d == 128) {
-    hipLaunchKernelGGL((k_attn<T, 128>), grid, block, 0, s, q, out, ldo, pg, tt, cross ? 1 : 0, n_qt, n_tasks);
-  } else if (pg.d == 64) {
-    hipLaunchKernelGGL((k_attn<T, 64>), grid, block, 0, s, q, out, ldo, pg, tt, cross ? 1 : 0, n_qt, n_tasks);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (pg.d == 128) return launch_attention_hd<T, 128>(cross, q, out, ldo, pg, tt, n_tasks, s);
+  if (pg.d == 64) return launch_attention_hd<T, 64>(cross, q, out, ldo, pg, tt, n_tasks, s);
+  return hipErrorInvalidValue;
 }
 
 template hipError_t launch_attention<bf16>(bool, const bf16*, bf16*, int, const PoolGeo&, const DevTask*,
