@@ -90,6 +90,62 @@ def setup_stage(cfg, n_tasks, seed=0):
     return dict(pool=pool, blk=blk, te=te, x=x, h=h, xe=xe, w=w, tw=tw)
 
 
+def run_stagger_bench(cfg, measured=64):
+    """Steady-state chunk interval of one stream under the staggered schedule
+    (all blocks, all steps, k chunks per step per tick): `measured` chunks
+    completed after a warm-up of S + W + 2 ticks, from events recorded after
+    each tick's Euler step."""
+    import torch
+    from autoregressive_denoising_dit_amd import runtime
+    from autoregressive_denoising_dit_amd.schedule import StaggeredRunner
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    D, F, H, d, B, S, W, k = cfg.hidden, cfg.ffn, cfg.heads, cfg.head_dim, cfg.n_blocks, cfg.n_steps, cfg.window, cfg.k
+
+    def rn(*shape, dtype=torch.float32, std=0.02):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(dtype).contiguous()
+
+    _log(f"setting up {cfg.name}: {B} blocks x {S} steps, k = {k}")
+    blocks, keep = [], []
+    pool = runtime.Pool(1, B, S, W + k, cfg.grid, H, d, cfg.n_ctx, runtime.ps_dtype(cfg.dtype))
+    for b in range(B):
+        w = {"wqkv": rn(3 * D, D, dtype=td), "wo": rn(D, D, dtype=td), "wq2": rn(D, D, dtype=td),
+             "wkv2": rn(2 * D, D, dtype=td), "wo2": rn(D, D, dtype=td), "w1": rn(F, D, dtype=td),
+             "w2": rn(D, F, dtype=td), "bqkv": rn(3 * D), "bo": rn(D), "bq2": rn(D), "bkv2": rn(2 * D),
+             "bo2": rn(D), "b1": rn(F), "b2": rn(D), "tmod": rn(6, D)}
+        blk = runtime.Block(w, D, H, d, F, b, runtime.ps_dtype(cfg.dtype))
+        pool.context_set(blk, 0, rn(cfg.n_ctx, D, dtype=td, std=1.0))
+        blocks.append(blk)
+        keep.append(w)
+    tw = {"wt1": rn(D, 256), "bt1": rn(D), "wt2": rn(D, D), "bt2": rn(D), "wp": rn(6 * D, D), "bp": rn(6 * D)}
+    te = runtime.TimeEmbed(tw, D, capacity=16)
+    runner = StaggeredRunner(pool, blocks, te, cfg.timesteps, W, k, 1)
+    tau0 = S + W + 2                       # warm-up ticks (pipeline filled, full windows)
+    tau1 = tau0 + (measured + k - 1) // k  # each later tick completes k chunks
+    n_chunks = k * (tau1 + 1)
+    x = rn(n_chunks, 1, cfg.tokens, D, std=1.0)
+    from autoregressive_denoising_dit_amd import _lib
+    torch.cuda.synchronize()
+    ev = {}
+    for tau in range(tau1 + 1):
+        if tau == tau0 + 1:
+            _lib.trace_enable(True)
+        runner.run_tick(tau, x, n_chunks)
+        if tau >= tau0:
+            ev[tau] = torch.cuda.Event(enable_timing=True)
+            ev[tau].record()
+    torch.cuda.synchronize()
+    trace = _lib.trace_read()
+    _lib.trace_enable(False)
+    assert torch.isfinite(x).all().item(), "non-finite latents"
+    done = k * (tau1 - tau0)
+    interval = ev[tau0].elapsed_time(ev[tau1]) / done
+    tick = ev[tau0].elapsed_time(ev[tau1]) / (tau1 - tau0)
+    per_tick = {n: round(ms / (tau1 - tau0), 3) for n, (_, ms) in trace.items()}
+    return interval, tick, done, per_tick
+
+
 def stage_tasks(cfg, n_tasks, tau, base_chunk=100):
     """Task i: stream i at step (tau + i) mod S, a steady-state chunk with a full window."""
     from autoregressive_denoising_dit_amd import runtime
@@ -271,7 +327,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c5", "c3", "c4"],
+                    help="c5 (default) / c2: one stage batch per step; c3 / c4: the staggered schedule "
+                         "over all blocks and steps, reporting the chunk interval")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -292,6 +350,22 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload in ("c3", "c4"):
+        cfg = get(args.workload)
+        interval, tick, done, per_tick = run_stagger_bench(cfg)
+        per_chunk = cfg.n_blocks * cfg.n_steps * stage_flops(cfg, cfg.window)
+        print(json.dumps({
+            "metric": "steady-state chunk interval (ms), staggered schedule, one stream",
+            "value": round(interval, 3), "unit": "ms", "n_gpus": 1, "higher_is_better": False,
+            "dtype": cfg.dtype, "data": "synthetic (seeded random-init weights, N(0,1) latents and contexts)",
+            "config": {"workload": cfg.name, "blocks": cfg.n_blocks, "steps": cfg.n_steps, "k": cfg.k,
+                       "window": cfg.window, "tokens_per_chunk": cfg.tokens, "hidden": cfg.hidden},
+            "chunks_measured": done, "tick_ms": round(tick, 3),
+            "stage_tasks_per_s": round(cfg.n_blocks * cfg.n_steps * cfg.k / (tick * 1e-3), 1),
+            "mfma_frac": round(per_chunk / (interval * 1e-3) / PEAK[cfg.dtype], 4),
+            "kernel_ms_per_tick": per_tick,
+        }), flush=True)
         return
     cfg = get(args.workload)
     n_tasks = cfg.batch
