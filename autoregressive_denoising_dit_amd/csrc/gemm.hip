@@ -43,6 +43,7 @@ constexpr int OPER_BYTES = NSTAGE * STAGE_CH * 16;      // 2 x 64 KB
 constexpr int STAGE_BYTES = 4 * 128 * EP * 4;          // 4 waves x 128 rows x pitch
 constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
 constexpr int TAB_BYTES = 160 * 1024 - SMEM_BYTES;     // LDS side tables of the epilogues
+constexpr int TAB_BIAS = 512, TAB_DATA = TAB_BIAS + BN * 4;   // table offsets (bytes)
 
 
 
@@ -61,10 +62,14 @@ __device__ __forceinline__ float gelu_tanh(float z) {
 // 64 columns at a time (row pitch EP floats), and stores it with lanes that
 // own 4 consecutive columns (16 lanes per row, 4 rows per instruction), so
 // that every global access is a 16-byte (fp32) or 8-byte (bf16) vector and
-// rows are contiguous runs.  Per-row side data that would otherwise be
-// fetched from memory row by row -- the pool offset of each task's write slot,
-// the RoPE cos/sin tables, the gate rows of the modulation -- is copied into
-// LDS before the k-loop, so the epilogue waits only on LDS.
+// rows are contiguous runs.  Side data that would otherwise be fetched from
+// memory during the epilogue -- the tile's bias columns, the pool offset of
+// each task's write slot, the RoPE cos/sin tables, the gate rows of the
+// modulation -- is copied into LDS before the k-loop.  A global load issued
+// after the epilogue's first stores would wait for those stores as well (one
+// in-order counter covers both), so the epilogue reads side data from LDS
+// only, and the residual epilogue issues each batch of residual loads before
+// the previous batch's stores.
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, f32x4 v) {
@@ -79,8 +84,9 @@ __device__ __forceinline__ void store4(T* p, f32x4 v) {
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 // LDS side tables: bytes [0, 256) the pool offset (elements) of each task's
-// write slot, [256, 512) a TabGeo, [512, TAB_BYTES) the data -- RoPE tables
-// (float2) for the QKV epilogue, gate rows (float) for the residual one.
+// write slot, [256, 512) a TabGeo, [512, 1536) the bias of the tile's 256
+// columns (zeros past N), [1536, TAB_BYTES) the data -- RoPE tables (float2)
+// for the QKV epilogue, gate rows (float) for the residual one.
 struct TabGeo {
   int t0;                      // first task (row block) the tile touches
   int off_f, off_y, off_x;     // RoPE tables in float2 units from byte 512
@@ -112,7 +118,8 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
   const int rq = lane >> 4, cq = lane & 15;   // row within a step of 4, column quad
   const int col = cbase + 4 * cq;
   const bool col_ok = col < N;                // N is a multiple of 4
-  const f32x4 bias = col_ok ? ld4(ep.bias + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float* btab = reinterpret_cast<const float*>(tab + TAB_BIAS) - n0;   // indexed by column
+  const f32x4 bias = ld4(btab + col);
 
   if constexpr (EPI == EPI_QKV || EPI == EPI_CTX_KV) {
     const int D = pg.H * pg.d;
@@ -138,7 +145,7 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
           vt = static_cast<T*>(ep.ctx_base) + (size_t)pg.H * pg.max_ctx * pg.d;
         }
         for (int c0 = 0; c0 < ncol; c0 += 4) {
-          const f32x4 v = ld4(stg + min(rr, 127) * EP + c0) + ld4(ep.bias + cbase + c0);
+          const f32x4 v = ld4(stg + min(rr, 127) * EP + c0) + ld4(btab + cbase + c0);
           const int cc = cbase + c0 - part * D;
           const int hh = cc >> ep.d_shift, dd = cc & (pg.d - 1);
           if (row_ok) {
@@ -163,7 +170,7 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
     } else {
       const TabGeo& tg = *reinterpret_cast<const TabGeo*>(tab + 256);
       RopePtrs lt;
-      const float2* tb2 = reinterpret_cast<const float2*>(tab + 512);
+      const float2* tb2 = reinterpret_cast<const float2*>(tab + TAB_DATA);
       lt.f = tb2 + tg.off_f;
       lt.y = tb2 + tg.off_y;
       lt.x = tb2 + tg.off_x;
@@ -202,33 +209,6 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
       }
       return;
     }
-  } else if constexpr (EPI == EPI_RES) {
-    // h_out = h_in + gate * (acc + bias); the residual rows are loaded EB steps
-    // ahead of their use so that their latency overlaps
-    constexpr int EB = 8;
-    const float* gtab = reinterpret_cast<const float*>(tab + 512);
-    const int t0 = reinterpret_cast<const TabGeo*>(tab + 256)->t0;
-    for (int r0 = 0; r0 < nrows; r0 += 4 * EB) {
-      f32x4 hv[EB];
-#pragma unroll
-      for (int k = 0; k < EB; ++k) {
-        const int r = min(r0 + 4 * k + rq, nrows - 1);
-        hv[k] = col_ok ? ld4(ep.h_in + (size_t)(rbase + r) * N + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
-#pragma unroll
-      for (int k = 0; k < EB; ++k) {
-        const int r = r0 + 4 * k + rq;
-        if (r >= nrows || !col_ok) continue;
-        const int row = rbase + r;
-        f32x4 gv = {1.0f, 1.0f, 1.0f, 1.0f};
-        if (ep.gate_row >= 0) {
-          const int tl = (int)ep.div_L.div(row) - t0;
-          gv = ld4(gtab + tl * BN + (col - n0));
-        }
-        const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
-        *reinterpret_cast<f32x4*>(ep.h_out + (size_t)row * N + col) = hv[k] + gv * v;
-      }
-    }
   } else {
     for (int r = rq; r < nrows; r += 4) {
       const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
@@ -245,13 +225,69 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
   }
 }
 
+// Gated residual epilogue of one wave over its whole 128 x 128 block:
+// h_out = h_in + gate * (acc + bias).  The block goes through the staging
+// area in two halves of 64 columns; the residual rows are read in batches of
+// 4 * EB rows, each batch loaded before the previous batch is stored, so that
+// a load never waits for earlier stores.
+template <int EB>
+__device__ __forceinline__ void load_res(f32x4 (&h)[EB], const float* h_in, int rbase, int nrows, int r0, int rq,
+                                         int col, int N) {
+#pragma unroll
+  for (int k = 0; k < EB; ++k) {
+    const int r = min(r0 + 4 * k + rq, nrows - 1);
+    h[k] = col < N ? ld4(h_in + (size_t)(rbase + r) * N + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+}
+
+template <typename StageFn>
+__device__ __forceinline__ void epilogue_res(float* stg, StageFn stage_half, int rbase, int cbase, int lane, int M,
+                                             int N, const EpiArgs& ep, const char* tab, int n0) {
+  constexpr int EB = 8, RB = 4 * EB, NB = 128 / RB;   // rows per batch, batches per half
+  const int nrows = min(128, M - rbase);
+  if (nrows <= 0 || cbase >= N) return;
+  const int rq = lane >> 4, cq = lane & 15;
+  const float* btab = reinterpret_cast<const float*>(tab + TAB_BIAS) - n0;
+  const float* gtab = reinterpret_cast<const float*>(tab + TAB_DATA);
+  const int t0 = reinterpret_cast<const TabGeo*>(tab + 256)->t0;
+  // every batch runs (rows past nrows are clamped loads and skipped
+  // stores), so that batch n always lives in register set n % 2
+  f32x4 hv[2][EB];
+  stage_half(0);
+  load_res<EB>(hv[0], ep.h_in, rbase, nrows, 0, rq, cbase + 4 * cq, N);
+#pragma unroll
+  for (int n = 0; n < 2 * NB; ++n) {
+    const int hlf = n / NB, b = n % NB;
+    if (n == NB) stage_half(1);   // the wave's reads of half 0 are done (LDS accesses complete in order)
+    if (n + 1 < 2 * NB) {
+      const int nn = n + 1;
+      load_res<EB>(hv[nn & 1], ep.h_in, rbase, nrows, (nn % NB) * RB, rq, cbase + (nn / NB) * 64 + 4 * cq, N);
+    }
+    const int col = cbase + hlf * 64 + 4 * cq;
+    if (col >= N) continue;
+    const f32x4 bias = ld4(btab + col);
+#pragma unroll
+    for (int k = 0; k < EB; ++k) {
+      const int r = b * RB + 4 * k + rq;
+      if (r >= nrows) continue;
+      const int row = rbase + r;
+      f32x4 gv = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (ep.gate_row >= 0) {
+        const int tl = (int)ep.div_L.div(row) - t0;
+        gv = ld4(gtab + tl * BN + (col - n0));
+      }
+      const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
+      *reinterpret_cast<f32x4*>(ep.h_out + (size_t)row * N + col) = hv[n & 1][k] + gv * v;
+    }
+  }
+}
+
 template <typename T, int EPI>
 __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* __restrict__ B,
                                              int M, int N, int K, int lda, EpiArgs ep,
                                              const DevTask* __restrict__ tasks) {
   constexpr int BK = ROWB / sizeof(T);
-  constexpr bool kTab = EPI == EPI_QKV || EPI == EPI_RES;
-  __shared__ u32x4 smem[(SMEM_BYTES + (kTab ? TAB_BYTES : 0)) / 16];
+  __shared__ u32x4 smem[(SMEM_BYTES + TAB_BYTES) / 16];
   char* tab = reinterpret_cast<char*>(smem) + SMEM_BYTES;
 
   const int tid = threadIdx.x;
@@ -269,6 +305,11 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const int m0 = tm * BM, n0 = tn * BN;
 
   // epilogue side tables (read only after the k-loop's barriers)
+  if (tid < BN / 4) {
+    const int c = n0 + 4 * tid;
+    reinterpret_cast<f32x4*>(tab + TAB_BIAS)[tid] =
+        c < N && ep.bias ? ld4(ep.bias + c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   if constexpr (EPI == EPI_QKV) {
     const PoolGeo& pg = ep.pool;
     const int n_tasks = (int)pg.div_L.div(M - 1) + 1;
@@ -289,7 +330,7 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
       tg->off_x = nf + ny;
     }
     if (ep.rope_tab) {
-      float2* d2 = reinterpret_cast<float2*>(tab + 512);
+      float2* d2 = reinterpret_cast<float2*>(tab + TAB_DATA);
       const float2* f0 = ep.rope_f + (size_t)t0 * pg.frames * (pg.seg_f / 2);
       for (int i = tid; i < nf + ny + nx; i += NT)
         d2[i] = i < nf ? f0[i] : i < nf + ny ? pg.rope_y[i - nf] : pg.rope_x[i - nf - ny];
@@ -299,7 +340,7 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
       const int t0 = (int)ep.div_L.div(m0);
       const int t1 = (int)ep.div_L.div(min(M, m0 + BM) - 1);
       if (tid == 0) reinterpret_cast<TabGeo*>(tab + 256)->t0 = t0;
-      float* gt = reinterpret_cast<float*>(tab + 512);
+      float* gt = reinterpret_cast<float*>(tab + TAB_DATA);
       for (int i = tid; i < (t1 - t0 + 1) * (BN / 4); i += NT) {
         const int t = t0 + i / (BN / 4), c4 = (i % (BN / 4)) * 4;
         const f32x4 v = n0 + c4 < N ? ld4(ep.mod + ((size_t)t * 6 + ep.gate_row) * N + n0 + c4)
@@ -426,11 +467,10 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
+  // each wave stages into and reads back its own region only; LDS accesses
+  // of one wave complete in order, so no barrier is needed between halves
   float* stg = reinterpret_cast<float*>(smem) + wave * (128 * EP);
-#pragma unroll
-  for (int hlf = 0; hlf < 2; ++hlf) {
-    // each wave stages into and reads back its own region only; LDS accesses
-    // of one wave complete in order, so no barrier is needed between halves
+  auto stage_half = [&](int hlf) __attribute__((always_inline)) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -440,7 +480,15 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
           const int row = i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
           stg[row * EP + jj * 32 + l32] = acc[i][2 * hlf + jj][r];
         }
-    epilogue_block<T, EPI>(stg, m0 + wm * 128, n0 + wn * 128 + hlf * 64, lane, M, N, ep, tab, n0);
+  };
+  if constexpr (EPI == EPI_RES) {
+    epilogue_res(stg, stage_half, m0 + wm * 128, n0 + wn * 128, lane, M, N, ep, tab, n0);
+  } else {
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      stage_half(hlf);
+      epilogue_block<T, EPI>(stg, m0 + wm * 128, n0 + wn * 128 + hlf * 64, lane, M, N, ep, tab, n0);
+    }
   }
 }
 
@@ -452,7 +500,8 @@ hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, i
   // 32-bit buffer offsets: every operand byte (plus one tile of overrun) must be addressable
   const uint64_t lim = 1ull << 32;
   if ((uint64_t)(M + BM) * lda * sizeof(T) >= lim || (uint64_t)(N + BN) * K * sizeof(T) >= lim ||
-      K % (ROWB / (int)sizeof(T)) != 0 || M <= 0 || N <= 0 || lda < K || (lda * sizeof(T)) % 16 != 0)
+      K % (ROWB / (int)sizeof(T)) != 0 || M <= 0 || N <= 0 || N % 4 != 0 || lda < K ||
+      (lda * sizeof(T)) % 16 != 0)
     return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid(tiles), block(NT);
@@ -462,12 +511,12 @@ hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, i
     const int L = epi == EPI_QKV ? ep.pool.L : ep.L;
     if (L < 64) return hipErrorInvalidValue;
     const int span = BM / L + 2;
-    if (epi == EPI_RES && span * BN * 4 > TAB_BYTES - 512) return hipErrorInvalidValue;
+    if (epi == EPI_RES && span * BN * 4 > TAB_BYTES - TAB_DATA) return hipErrorInvalidValue;
     if (epi == EPI_QKV) {
       const PoolGeo& pg = ep.pool;
       const int64_t pairs = (int64_t)span * pg.frames * (pg.seg_f / 2) + (int64_t)pg.rows * (pg.seg_h / 2) +
                             (int64_t)pg.cols * (pg.seg_w / 2);
-      e.rope_tab = pairs * 8 <= TAB_BYTES - 512 ? 1 : 0;
+      e.rope_tab = pairs * 8 <= TAB_BYTES - TAB_DATA ? 1 : 0;
       if (M / L > 32) return hipErrorInvalidValue;   // one write-slot offset per task
     }
   }
