@@ -26,6 +26,7 @@ import sys
 import time
 
 PEAK = {"bf16": 2516.6e12, "fp32": 157.3e12}   # dense MFMA, 256 CU x 2.4 GHz
+MI355X_XCDS, MI355X_SIMDS = 8, 256 * 4          # accelerator dies, SIMDs (4 per CU)
 HBM_PEAK = 8.0e12
 
 
@@ -264,6 +265,12 @@ def pmc_summary(dirs):
         for c in list(agg):
             if c != "dispatches":
                 agg[c] = round(agg[c] / n, 3)
+        # Matrix-core utilisation: SQ_VALU_MFMA_BUSY_CYCLES sums busy cycles over
+        # all SIMDs; GRBM_GUI_ACTIVE sums the GPU's active cycles over the XCDs.
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in agg and agg.get("GRBM_GUI_ACTIVE"):
+            cyc = agg["GRBM_GUI_ACTIVE"] / MI355X_XCDS
+            agg["mfma_busy_frac"] = round(agg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * MI355X_SIMDS), 4)
+            agg["active_cycles_per_xcd"] = round(cyc)
     print(json.dumps(out, indent=1, sort_keys=True), flush=True)
 
 
