@@ -8,7 +8,10 @@
 // "三层设计", layer 2).
 //
 // Tiling: 256 x 256 macro tile, 4 waves in a 2 x 2 grid, each owning a
-// 128 x 128 sub-tile = 4 x 4 MFMA 32x32 accumulators (in AGPRs).  K advances
+// 128 x 128 sub-tile = 4 x 4 MFMA 32x32 accumulators (in AGPRs); or, where it
+// fills the CUs' last round better, 192 x 256 tiles of 96 x 128 per wave
+// (3 x 4 accumulators).  Every output element sees the same MFMA sequence
+// over K either way, so the choice never changes a result.  K advances
 // in stages of 128 bytes per row (64 bf16 / 32 fp32 = four MFMA k-units)
 // through two LDS stages filled by memory-to-LDS copies.  Operand chunks are
 // XOR-swizzled so that fragment reads of consecutive rows hit distinct banks.
@@ -30,16 +33,24 @@ namespace ps {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, ROWB = 128, NT = 256;
+constexpr int BMX = 256, BN = 256, ROWB = 128, NT = 256;   // largest row tile, column tile
 constexpr int CPR = ROWB / 16;  // 16-byte chunks per LDS row (8)
 constexpr int NSTAGE = 2;       // LDS stages of operands
 constexpr int U = ROWB / 32;    // MFMA k-units per stage (4)
 constexpr int RPI = 64 / CPR;   // rows per copy instruction (8)
-constexpr int IPW = (BM / 4) / RPI;   // copy instructions per wave per operand per stage (8)
-constexpr int CPG = IPW / 4;    // copies per group of four MFMAs (2)
+constexpr int IPWB = (BN / 4) / RPI;   // B copy instructions per wave per stage (8)
 constexpr int EP = 68;          // fp32 row pitch of the epilogue staging (64 columns, 16-byte rows)
-constexpr int STAGE_CH = (BM + BN) * CPR;               // 16-byte chunks per stage
-constexpr int OPER_BYTES = NSTAGE * STAGE_CH * 16;      // 2 x 64 KB
+constexpr int OPER_BYTES = NSTAGE * (BMX + BN) * CPR * 16;   // 2 x 64 KB
+
+// Row tile with MI MFMA tiles (32 rows each) per wave and two waves down.
+template <int MI>
+struct RowTile {
+  static constexpr int BM = 64 * MI;                  // rows per tile
+  static constexpr int MR = 32 * MI;                  // rows per wave
+  static constexpr int IPWA = (BM / 4) / RPI;         // A copy instructions per wave per stage
+  static constexpr int STAGE_CH = (BM + BN) * CPR;    // 16-byte chunks per stage
+  static_assert(IPWA * RPI * 4 == BM, "row tile must split evenly over the copies");
+};
 constexpr int STAGE_BYTES = 4 * 128 * EP * 4;          // 4 waves x 128 rows x pitch
 constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
 constexpr int TAB_BYTES = 160 * 1024 - SMEM_BYTES;     // LDS side tables of the epilogues
@@ -107,12 +118,12 @@ struct RopePtrs {
   const float2* x;
 };
 
-// One wave's staged 128 x 64 block: rows rbase.., columns cbase.. of C.
-template <typename T, int EPI>
+// One wave's staged MR x 64 block: rows rbase.., columns cbase.. of C.
+template <typename T, int EPI, int MR>
 __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int cbase, int lane, int M, int N,
                                                const EpiArgs& ep, const char* tab, int n0) {
   if (cbase >= N) return;
-  const int nrows = min(128, M - rbase);
+  const int nrows = min(MR, M - rbase);
   if (nrows <= 0) return;
   const PoolGeo& pg = ep.pool;
   const int rq = lane >> 4, cq = lane & 15;   // row within a step of 4, column quad
@@ -145,7 +156,7 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
           vt = static_cast<T*>(ep.ctx_base) + (size_t)pg.H * pg.max_ctx * pg.d;
         }
         for (int c0 = 0; c0 < ncol; c0 += 4) {
-          const f32x4 v = ld4(stg + min(rr, 127) * EP + c0) + ld4(btab + cbase + c0);
+          const f32x4 v = ld4(stg + min(rr, MR - 1) * EP + c0) + ld4(btab + cbase + c0);
           const int cc = cbase + c0 - part * D;
           const int hh = cc >> ep.d_shift, dd = cc & (pg.d - 1);
           if (row_ok) {
@@ -225,7 +236,7 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
   }
 }
 
-// Gated residual epilogue of one wave over its whole 128 x 128 block:
+// Gated residual epilogue of one wave over its whole MR x 128 block:
 // h_out = h_in + gate * (acc + bias).  The block goes through the staging
 // area in two halves of 64 columns; the residual rows are read in batches of
 // 4 * EB rows, each batch loaded before the previous batch is stored, so that
@@ -240,11 +251,11 @@ __device__ __forceinline__ void load_res(f32x4 (&h)[EB], const float* h_in, int 
   }
 }
 
-template <typename StageFn>
+template <int MR, typename StageFn>
 __device__ __forceinline__ void epilogue_res(float* stg, StageFn stage_half, int rbase, int cbase, int lane, int M,
                                              int N, const EpiArgs& ep, const char* tab, int n0) {
-  constexpr int EB = 8, RB = 4 * EB, NB = 128 / RB;   // rows per batch, batches per half
-  const int nrows = min(128, M - rbase);
+  constexpr int EB = 8, RB = 4 * EB, NB = MR / RB;   // rows per batch, batches per half
+  const int nrows = min(MR, M - rbase);
   if (nrows <= 0 || cbase >= N) return;
   const int rq = lane >> 4, cq = lane & 15;
   const float* btab = reinterpret_cast<const float*>(tab + TAB_BIAS) - n0;
@@ -282,11 +293,13 @@ __device__ __forceinline__ void epilogue_res(float* stg, StageFn stage_half, int
   }
 }
 
-template <typename T, int EPI>
+template <typename T, int EPI, int MI>
 __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* __restrict__ B,
                                              int M, int N, int K, int lda, EpiArgs ep,
                                              const DevTask* __restrict__ tasks) {
   constexpr int BK = ROWB / sizeof(T);
+  constexpr int BM = RowTile<MI>::BM, MR = RowTile<MI>::MR, IPWA = RowTile<MI>::IPWA;
+  constexpr int STAGE_CH = RowTile<MI>::STAGE_CH;
   __shared__ u32x4 smem[(SMEM_BYTES + TAB_BYTES) / 16];
   char* tab = reinterpret_cast<char*>(smem) + SMEM_BYTES;
 
@@ -364,27 +377,33 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const i32x4 rsb = {(int)(uint32_t)b_base, (int)(uint32_t)(b_base >> 32), (int)((size_t)N * K * sizeof(T)),
                      0x00020000};
   const uint32_t a_row = (uint32_t)lda * sizeof(T), b_row = (uint32_t)K * sizeof(T);
-  uint32_t voa[IPW], vob[IPW];
+  uint32_t voa[IPWA], vob[IPWB];
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int row = (wave * IPW + i) * RPI + lane / CPR;
+  for (int i = 0; i < IPWA; ++i) {
+    const int row = (wave * IPWA + i) * RPI + lane / CPR;
     const int cl = (lane % CPR) ^ lds_swz<CPR>(row);
     voa[i] = (uint32_t)(m0 + row) * a_row + cl * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < IPWB; ++i) {
+    const int row = (wave * IPWB + i) * RPI + lane / CPR;
+    const int cl = (lane % CPR) ^ lds_swz<CPR>(row);
     vob[i] = (uint32_t)(n0 + row) * b_row + cl * 16;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const uint32_t wblk = (uint32_t)__builtin_amdgcn_readfirstlane(wave * IPW * 1024);
-  // copy instruction c of stage kt: c < IPW are A blocks, the rest B blocks
+  const uint32_t wblk_a = (uint32_t)__builtin_amdgcn_readfirstlane(wave * IPWA * 1024);
+  const uint32_t wblk_b = (uint32_t)__builtin_amdgcn_readfirstlane(BM * ROWB + wave * IPWB * 1024);
+  // copy instruction c of stage kt: c < IPWA are A blocks, the rest B blocks
   auto dma_one = [&](int kt, int c) __attribute__((always_inline)) {
-    const uint32_t dst = lds0 + (kt & (NSTAGE - 1)) * (STAGE_CH * 16) + wblk;
+    const uint32_t dst = lds0 + (kt & (NSTAGE - 1)) * (STAGE_CH * 16);
     const uint32_t koff = (uint32_t)kt * ROWB;
-    if (c < IPW) lds_dma16_buf(rsa, voa[c], koff, dst + c * 1024);
-    else lds_dma16_buf(rsb, vob[c - IPW], koff, dst + BM * ROWB + (c - IPW) * 1024);
+    if (c < IPWA) lds_dma16_buf(rsa, voa[c], koff, dst + wblk_a + c * 1024);
+    else lds_dma16_buf(rsb, vob[c - IPWA], koff, dst + wblk_b + (c - IPWA) * 1024);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -393,16 +412,17 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const int wm = wave >> 1, wn = wave & 1;
   const int fsw = lds_swz<CPR>(l32);
   u32x4 fr[2][8];   // MFMA fragments of two k-units (A 0..3, B 4..7)
-  // One k-unit: 16 MFMAs on fragment set ms in four groups of four.  Each
-  // group also reads two fragments of the next k-unit (set fs, LDS buffer
-  // fbuf, unit fu: the four B fragments first, as every group of the next
-  // unit needs them, then A in order) and issues CPG copy instructions of
-  // operand half dh of stage dkt (none when dkt < 0).
+  // One k-unit: 4 MI MFMAs on fragment set ms in MI groups of four.  The
+  // groups also read the fragments of the next k-unit (set fs, LDS buffer
+  // fbuf, unit fu: the four B fragments first, two per group, as every group
+  // of the next unit needs them, then A in order) and issue the copy
+  // instructions of operand dh (0 = A, 1 = B) of stage dkt, spread evenly
+  // (none when dkt < 0).
   auto unit = [&](int ms, int fs, int fbuf, int fu, bool rd, int dkt, int dh) __attribute__((always_inline)) {
     const u32x4* st = smem + fbuf * STAGE_CH;
     const int ch = (2 * fu + g) ^ fsw;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) Mfma<T>::unit(acc[i][j], fr[ms][i], fr[ms][4 + j]);
       if (rd) {
@@ -410,18 +430,25 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
           fr[fs][4 + 2 * i] = st[(BM + wn * 128 + (2 * i) * 32 + l32) * CPR + ch];
           fr[fs][5 + 2 * i] = st[(BM + wn * 128 + (2 * i + 1) * 32 + l32) * CPR + ch];
         } else {
-          fr[fs][2 * (i - 2)] = st[(wm * 128 + (2 * (i - 2)) * 32 + l32) * CPR + ch];
-          fr[fs][2 * (i - 2) + 1] = st[(wm * 128 + (2 * (i - 2) + 1) * 32 + l32) * CPR + ch];
+          // A fragments [a0, a1) of the next unit in group i
+          const int a0 = (i - 2) * MI / (MI - 2), a1 = (i - 1) * MI / (MI - 2);
+#pragma unroll
+          for (int a = a0; a < a1; ++a) fr[fs][a] = st[(wm * MR + a * 32 + l32) * CPR + ch];
         }
       }
-      if (dkt >= 0)
+      if (dkt >= 0) {
+        const int n = dh ? IPWB : IPWA;
+        const int c0 = i * n / MI, c1 = (i + 1) * n / MI;
 #pragma unroll
-        for (int c = 0; c < CPG; ++c) dma_one(dkt, dh * IPW + i * CPG + c);
+        for (int c = c0; c < c1; ++c) dma_one(dkt, dh * IPWA + c);
+      }
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -451,12 +478,18 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   const int nk = K / BK;
   for (int st = 0; st < NSTAGE && st < nk; ++st)
 #pragma unroll
-    for (int c = 0; c < 2 * IPW; ++c) dma_one(st, c);
-  if (nk > 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // stage 0 landed, stage 1 may fly
+    for (int c = 0; c < IPWA + IPWB; ++c) dma_one(st, c);
+  static_assert(IPWA + IPWB == 14 || IPWA + IPWB == 16, "prologue wait counts 14 or 16 copies");
+  if (nk > 1) {   // stage 0 landed, stage 1 may fly
+    if constexpr (IPWA + IPWB == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+  }
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) fr[0][i] = smem[((i < 4 ? wm * 128 + i * 32 : BM + wn * 128 + (i - 4) * 32) + l32) * CPR + (g ^ fsw)];
+  for (int i = 0; i < 8; ++i)
+    if (i < MI || i >= 4)
+      fr[0][i] = smem[((i < 4 ? wm * MR + i * 32 : BM + wn * 128 + (i - 4) * 32) + l32) * CPR + (g ^ fsw)];
   int kt = 0;
   if (nk > 1) {
     stage(0, false, nk > 2, false);
@@ -474,7 +507,7 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = i * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
@@ -482,27 +515,35 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
         }
   };
   if constexpr (EPI == EPI_RES) {
-    epilogue_res(stg, stage_half, m0 + wm * 128, n0 + wn * 128, lane, M, N, ep, tab, n0);
+    epilogue_res<MR>(stg, stage_half, m0 + wm * MR, n0 + wn * 128, lane, M, N, ep, tab, n0);
   } else {
 #pragma unroll
     for (int hlf = 0; hlf < 2; ++hlf) {
       stage_half(hlf);
-      epilogue_block<T, EPI>(stg, m0 + wm * 128, n0 + wn * 128 + hlf * 64, lane, M, N, ep, tab, n0);
+      epilogue_block<T, EPI, MR>(stg, m0 + wm * MR, n0 + wn * 128 + hlf * 64, lane, M, N, ep, tab, n0);
     }
   }
 }
 
 }  // namespace
 
-template <typename T>
-hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, int K, const EpiArgs& ep,
-                       const DevTask* tt, hipStream_t s) {
-  // 32-bit buffer offsets: every operand byte (plus one tile of overrun) must be addressable
-  const uint64_t lim = 1ull << 32;
-  if ((uint64_t)(M + BM) * lda * sizeof(T) >= lim || (uint64_t)(N + BN) * K * sizeof(T) >= lim ||
-      K % (ROWB / (int)sizeof(T)) != 0 || M <= 0 || N <= 0 || N % 4 != 0 || lda < K ||
-      (lda * sizeof(T)) % 16 != 0)
-    return hipErrorInvalidValue;
+// Compute units of the current device, read once per device.
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] <= 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+template <typename T, int MI>
+static hipError_t launch_gemm_mi(int epi, const T* A, int lda, const T* B, int M, int N, int K, const EpiArgs& ep,
+                                 const DevTask* tt, hipStream_t s) {
+  constexpr int BM = RowTile<MI>::BM;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid(tiles), block(NT);
   // LDS side tables of the epilogue: a tile's rows span at most BM / L + 2 tasks
@@ -521,14 +562,34 @@ hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, i
     }
   }
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((k_gemm<T, EPI_QKV>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
-    case EPI_CTX_KV: hipLaunchKernelGGL((k_gemm<T, EPI_CTX_KV>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
-    case EPI_STORE: hipLaunchKernelGGL((k_gemm<T, EPI_STORE>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
-    case EPI_GELU: hipLaunchKernelGGL((k_gemm<T, EPI_GELU>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
-    case EPI_RES: hipLaunchKernelGGL((k_gemm<T, EPI_RES>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemm<T, EPI_QKV, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_CTX_KV: hipLaunchKernelGGL((k_gemm<T, EPI_CTX_KV, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_STORE: hipLaunchKernelGGL((k_gemm<T, EPI_STORE, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_GELU: hipLaunchKernelGGL((k_gemm<T, EPI_GELU, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_RES: hipLaunchKernelGGL((k_gemm<T, EPI_RES, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, int K, const EpiArgs& ep,
+                       const DevTask* tt, hipStream_t s) {
+  // 32-bit buffer offsets: every operand byte (plus one tile of overrun) must be addressable
+  const uint64_t lim = 1ull << 32;
+  if ((uint64_t)(M + BMX) * lda * sizeof(T) >= lim || (uint64_t)(N + BN) * K * sizeof(T) >= lim ||
+      K % (ROWB / (int)sizeof(T)) != 0 || M <= 0 || N <= 0 || N % 4 != 0 || lda < K ||
+      (lda * sizeof(T)) % 16 != 0)
+    return hipErrorInvalidValue;
+  // Row tile: the one with the shorter estimated run, in rounds of tiles
+  // over all CUs.  A round of 192-row tiles measured 0.82-0.91 of a round of
+  // 256-row ones (fewer rows per copied byte); it is counted as 0.85 (17/20).
+  // Ties keep 256 rows.
+  const int cu = cu_count(), tn = (N + BN - 1) / BN;
+  auto rounds = [&](int bm) { return (int64_t)((((M + bm - 1) / bm) * tn + cu - 1) / cu); };
+  if (rounds(RowTile<3>::BM) * 17 < rounds(RowTile<4>::BM) * 20)
+    return launch_gemm_mi<T, 3>(epi, A, lda, B, M, N, K, ep, tt, s);
+  return launch_gemm_mi<T, 4>(epi, A, lda, B, M, N, K, ep, tt, s);
 }
 
 template hipError_t launch_gemm<bf16>(int, const bf16*, int, const bf16*, int, int, int, const EpiArgs&,
