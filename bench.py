@@ -14,8 +14,11 @@ timed region starts.
 
 Prints one JSON line: stage tasks/s, ms per step, the steady-state chunk
 interval, the fraction of the bf16 MFMA peak, a roofline record of the
-dominant kernel (HIP-event timing inside the timed region) and the CPU oracle
-timed on a bounded sample of the same workload.
+dominant kernel and the CPU oracle timed on a bounded sample of the same
+workload.  The timed steps run without per-kernel events; the same number of
+steps then runs again with a HIP event pair around every kernel (recorded by
+the library on the kernel's stream), which gives the per-kernel durations and
+the roofline record's.
 """
 from __future__ import annotations
 
@@ -95,7 +98,8 @@ def run_stagger_bench(cfg, measured=64):
     """Steady-state chunk interval of one stream under the staggered schedule
     (all blocks, all steps, k chunks per step per tick): `measured` chunks
     completed after a warm-up of S + W + 2 ticks, from events recorded after
-    each tick's Euler step."""
+    each tick's Euler step.  As many further ticks then run with per-kernel
+    events, for the time per tick of each kernel."""
     import torch
     from autoregressive_denoising_dit_amd import runtime
     from autoregressive_denoising_dit_amd.schedule import StaggeredRunner
@@ -124,16 +128,18 @@ def run_stagger_bench(cfg, measured=64):
     runner = StaggeredRunner(pool, blocks, te, cfg.timesteps, W, k, 1)
     tau0 = S + W + 2                       # warm-up ticks (pipeline filled, full windows)
     tau1 = tau0 + (measured + k - 1) // k  # each later tick completes k chunks
-    n_chunks = k * (tau1 + 1)
+    tau2 = tau1 + (tau1 - tau0)            # then as many ticks again with per-kernel events
+    n_chunks = k * (tau2 + 1)
     x = rn(n_chunks, 1, cfg.tokens, D, std=1.0)
     from autoregressive_denoising_dit_amd import _lib
     torch.cuda.synchronize()
     ev = {}
-    for tau in range(tau1 + 1):
-        if tau == tau0 + 1:
+    for tau in range(tau2 + 1):
+        if tau == tau1 + 1:
+            torch.cuda.synchronize()
             _lib.trace_enable(True)
         runner.run_tick(tau, x, n_chunks)
-        if tau >= tau0:
+        if tau0 <= tau <= tau1:
             ev[tau] = torch.cuda.Event(enable_timing=True)
             ev[tau].record()
     torch.cuda.synchronize()
@@ -143,7 +149,7 @@ def run_stagger_bench(cfg, measured=64):
     done = k * (tau1 - tau0)
     interval = ev[tau0].elapsed_time(ev[tau1]) / done
     tick = ev[tau0].elapsed_time(ev[tau1]) / (tau1 - tau0)
-    per_tick = {n: round(ms / (tau1 - tau0), 3) for n, (_, ms) in trace.items()}
+    per_tick = {n: round(ms / (tau2 - tau1), 3) for n, (_, ms) in trace.items()}
     return interval, tick, done, per_tick
 
 
@@ -177,8 +183,7 @@ def run_stage_bench(cfg, n_tasks, steps, warmup):
 
     for tau in range(warmup):
         step(tau)
-    torch.cuda.synchronize()
-    _lib.trace_enable(True)
+    # timed region: no per-kernel events (they add a gap between kernels)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -188,11 +193,17 @@ def run_stage_bench(cfg, n_tasks, steps, warmup):
         ev[tau + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    trace = _lib.trace_read()
-    _lib.trace_enable(False)
     assert torch.isfinite(st["h"]).all().item(), "non-finite stage output"
     sec = (t1 - t0) / steps
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    # the same steps again with a HIP event pair around every kernel, recorded
+    # by the library on the stream the kernel runs on: per-kernel durations
+    _lib.trace_enable(True)
+    for tau in range(steps):
+        step(tau)
+    torch.cuda.synchronize()
+    trace = _lib.trace_read()
+    _lib.trace_enable(False)
     return sec, trace, per_step
 
 
