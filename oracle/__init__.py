@@ -2,7 +2,8 @@
 
 A plain, slow, float64 NumPy statement of what one stage task computes (one DiT
 Transformer block at one denoising step for one latent chunk, reading the noisy
-KV that earlier chunks left at that same step) and of the two chunk x step
+KV that earlier chunks left at that same step), of the patch embedding and
+output head either side of the block stack, and of the two chunk x step
 schedules (sequential, staggered).  It shares no code with the HIP path; only
 the seeded generators in ``synthetic`` serve both.
 
@@ -20,4 +21,5 @@ from .block import (  # noqa: F401
     qkv_phase, rest_phase, rope3d, rope_segments, silu, sinusoid, time_embedding,
     token_positions,
 )
+from .head import output_head, patch_embed, patchify, time_mlp, unpatchify  # noqa: F401
 from .schedule import RingPool, run_schedule, staggered_ticks  # noqa: F401

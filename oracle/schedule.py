@@ -19,7 +19,9 @@ Because batching and staggering only reorder independent work, the two must
 give bitwise identical latents and caches; the tests assert exactly that.
 
 Euler step of flow matching: x^{s+1} = x^s - (t_s - t_{s+1}) v with
-t_S = 0 and v the output of the last block (v is the velocity prediction).
+t_S = 0 and v the velocity prediction: the output of the last block, or, with
+the patch embedding and output head, x holds the chunk's latent patches,
+h_0 = patch_embed(x) and v = output_head(h_B, u(t_s)) (``head.py``).
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ from typing import Callable, Dict, List, Sequence, Tuple
 import numpy as np
 
 from .block import F64, context_kv, modulation, qkv_phase, rest_phase, time_embedding
+from .head import output_head, patch_embed, time_mlp
 
 
 class SlotConflict(RuntimeError):
@@ -95,15 +98,19 @@ def _run_batch(tasks, b, w, E, h, pool, contexts_kv, cfg):
 def run_schedule(cfg, blocks: Sequence[dict], tw: dict,
                  latent: Callable[[int, int], np.ndarray],
                  contexts: Sequence[np.ndarray], n_chunks: int,
-                 order: str = "sequential", k: int = 1, n_slots: int | None = None):
+                 order: str = "sequential", k: int = 1, n_slots: int | None = None,
+                 head: dict | None = None):
     """Denoise ``n_chunks`` chunks of each stream through all steps and blocks.
 
     blocks: weights of blocks 0..B-1; tw: timestep-embedding weights;
-    latent(sigma, c): x^0 of a chunk; contexts[sigma]: conditioning tokens.
+    latent(sigma, c): x^0 of a chunk ([L, D] tokens, or [L, P] latent patches
+    when ``head`` -- patch embedding and output head weights -- is given);
+    contexts[sigma]: conditioning tokens.
     Returns (x_final dict (sigma, c) -> x^S, pool)."""
     S, B = cfg.n_steps, len(blocks)
     ts = list(cfg.timesteps) + [0.0]
     E = [time_embedding(t, tw) for t in cfg.timesteps]
+    U = [time_mlp(t, tw) for t in cfg.timesteps] if head is not None else None
     n_streams = len(contexts)
     contexts_kv = {(sg, b): context_kv(contexts[sg], blocks[b], cfg.heads)
                    for sg in range(n_streams) for b in range(B)}
@@ -121,9 +128,13 @@ def run_schedule(cfg, blocks: Sequence[dict], tw: dict,
         raise ValueError(order)
 
     for tasks in ticks:
-        h = {(sg, c): x[(sg, c)].copy() for (sg, c, s) in tasks}
+        if head is None:
+            h = {(sg, c): x[(sg, c)].copy() for (sg, c, s) in tasks}
+        else:
+            h = {(sg, c): patch_embed(x[(sg, c)], head) for (sg, c, s) in tasks}
         for b in range(B):
             _run_batch(tasks, b, blocks[b], E, h, pool, contexts_kv, cfg)
         for (sg, c, s) in tasks:
-            x[(sg, c)] = x[(sg, c)] - (ts[s] - ts[s + 1]) * h[(sg, c)]
+            v = h[(sg, c)] if head is None else output_head(h[(sg, c)], U[s], head)
+            x[(sg, c)] = x[(sg, c)] - (ts[s] - ts[s + 1]) * v
     return x, pool

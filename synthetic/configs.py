@@ -31,11 +31,25 @@ class StageConfig:
     n_streams: int = 1
     k: int = 1             # chunks of one stream entering a step per tick
     batch: int = 1         # tasks per ps_stage_batch call in the measured run
+    latent_channels: int = 16            # C of the latent video (patch embedding / output head)
+    patch: Tuple[int, int, int] = (1, 2, 2)   # latent frames x rows x cols per token
 
     @property
     def tokens(self) -> int:
         f, h, w = self.grid
         return f * h * w
+
+    @property
+    def latent_dim(self) -> int:
+        """P: latent values per token (channels x patch volume)."""
+        pf, ph, pw = self.patch
+        return self.latent_channels * pf * ph * pw
+
+    @property
+    def latent_shape(self) -> Tuple[int, int, int, int]:
+        """(C, frames, rows, cols) of one chunk's latent."""
+        (f, h, w), (pf, ph, pw) = self.grid, self.patch
+        return (self.latent_channels, f * pf, h * ph, w * pw)
 
     @property
     def n_steps(self) -> int:
@@ -50,7 +64,7 @@ class StageConfig:
 C1 = StageConfig(
     name="c1_tiny", hidden=128, heads=2, head_dim=64, ffn=512, grid=(1, 8, 8),
     window=2, n_ctx=16, n_blocks=2, timesteps=(1.0, 0.5), dtype="fp32",
-    n_streams=1, k=1, batch=2)
+    n_streams=1, k=1, batch=2, latent_channels=8)
 
 C2 = StageConfig(
     name="c2_wan13b_stage", hidden=1536, heads=12, head_dim=128, ffn=8960,
@@ -65,7 +79,7 @@ C3 = StageConfig(
 C4 = StageConfig(
     name="c4_wan22_5b_timeshared", hidden=3072, heads=24, head_dim=128, ffn=14336,
     grid=(1, 40, 44), window=3, n_ctx=512, n_blocks=30,
-    timesteps=(1.0, 0.75, 0.5, 0.25), dtype="bf16", n_streams=1, k=2, batch=8)
+    timesteps=(1.0, 0.75, 0.5, 0.25), dtype="bf16", n_streams=1, k=2, batch=8, latent_channels=48)
 
 C5 = StageConfig(
     name="c5_wan14b_stage16", hidden=5120, heads=40, head_dim=128, ffn=13824,

@@ -14,7 +14,8 @@ quantisation.  Latents stay fp32 (the residual stream is fp32).
 
 Layouts: linear weights are [in, out] (y = x @ W + b); the fused QKV weight is
 [D, 3D] with column blocks (q | k | v); the cross K/V weight is [D, 2D] with
-blocks (k | v); the per-block modulation table is [6, D].
+blocks (k | v); the per-block modulation table is [6, D]; the patch embedding
+is [P, D] and the output head [D, P] with a [2, D] modulation table.
 """
 from __future__ import annotations
 
@@ -75,6 +76,19 @@ def time_weights(cfg: StageConfig, seed: int = 0) -> Dict[str, np.ndarray]:
         "wp": (D, 6 * D), "bp": (6 * D,),
     }
     return {k: _draw(cfg, seed, "time." + k, s, WEIGHT_STD) for k, s in shapes.items()}
+
+
+def head_weights(cfg: StageConfig, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Patch embedding (P -> D) and output head (D -> P, modulation table [2, D])."""
+    D, P = cfg.hidden, cfg.latent_dim
+    shapes = {"w_embed": (P, D), "b_embed": (D,), "w_head": (D, P), "b_head": (P,), "t_head": (2, D)}
+    return {k: _draw(cfg, seed, "head." + k, s, WEIGHT_STD) for k, s in shapes.items()}
+
+
+def latent_patches(cfg: StageConfig, stream: int, chunk: int, seed: int = 0) -> np.ndarray:
+    """x^0 of one chunk as latent patches: [L, P] fp32 noise.  Stream sigma uses seed + sigma."""
+    return _draw(cfg, seed + stream, f"latent_patches.c{chunk}", (cfg.tokens, cfg.latent_dim), 1.0,
+                 rounded=False)
 
 
 def latent(cfg: StageConfig, stream: int, chunk: int, seed: int = 0) -> np.ndarray:
