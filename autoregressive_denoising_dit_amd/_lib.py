@@ -32,7 +32,7 @@ EXPORTS = (
     "ps_context_fetch", "ps_block_create", "ps_block_destroy", "ps_time_embed_create",
     "ps_time_embed_destroy", "ps_time_embed_get", "ps_context_set", "ps_stage_batch",
     "ps_euler_update", "ps_last_error", "ps_trace_enable", "ps_trace_collect", "ps_trace_count",
-    "ps_trace_entry",
+    "ps_trace_entry", "ps_head_create", "ps_head_destroy", "ps_patch_embed", "ps_output_head",
 )
 
 
@@ -57,6 +57,11 @@ class BlockDesc(C.Structure):
 class TimeDesc(C.Structure):
     _fields_ = ([("hidden", C.c_int32), ("capacity", C.c_int32)]
                 + [(n, C.c_void_p) for n in ("wt1", "bt1", "wt2", "bt2", "wp", "bp")])
+
+
+class HeadDesc(C.Structure):
+    _fields_ = ([("hidden", C.c_int32), ("latent_dim", C.c_int32), ("dtype", C.c_int32)]
+                + [(n, C.c_void_p) for n in ("w_embed", "w_head", "b_embed", "b_head", "t_head")])
 
 
 class Task(C.Structure):
@@ -93,6 +98,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ps_context_set": [vp, vp, i32, vp, i32, vp],
         "ps_stage_batch": [vp, vp, vp, C.POINTER(Task), i32, vp, vp, vp],
         "ps_euler_update": [vp, vp, C.POINTER(C.c_float), i32, i32, i32, i32, vp],
+        "ps_head_create": [C.POINTER(HeadDesc), C.POINTER(vp)],
+        "ps_head_destroy": [vp],
+        "ps_patch_embed": [vp, vp, vp, i32, vp],
+        "ps_output_head": [vp, vp, C.POINTER(C.c_float), i32, i32, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -211,7 +211,8 @@ struct ps_block {
 
 struct ps_time_embed {
   ps_time_desc d{};
-  float* cache = nullptr;      // [capacity][6][D]
+  float* cache = nullptr;      // [capacity][6][D]: e(t)
+  float* cache_u = nullptr;    // [capacity][D]: u(t), the timestep MLP output
   float* scratch = nullptr;    // 256 + 2 D floats
   std::vector<uint32_t> key;
   std::vector<uint64_t> used;
@@ -402,9 +403,11 @@ extern "C" ps_status ps_time_embed_create(const ps_time_desc* desc, ps_time_embe
   ps_time_embed* te = new ps_time_embed();
   te->d = d;
   if (hipMalloc(&te->cache, sizeof(float) * (size_t)d.capacity * 6 * d.hidden) != hipSuccess ||
+      hipMalloc(&te->cache_u, sizeof(float) * (size_t)d.capacity * d.hidden) != hipSuccess ||
       hipMalloc(&te->scratch, sizeof(float) * (PS_FREQ_DIM + 2 * (size_t)d.hidden)) != hipSuccess) {
     (void)hipGetLastError();
     if (te->cache) (void)hipFree(te->cache);
+    if (te->cache_u) (void)hipFree(te->cache_u);
     delete te;
     return fail(PS_ERR_OUT_OF_MEMORY, "time embed: cannot allocate cache");
   }
@@ -419,6 +422,7 @@ extern "C" ps_status ps_time_embed_destroy(ps_time_embed* te) {
   if (!te) return fail(PS_ERR_INVALID_ARG, "ps_time_embed_destroy: null handle");
   (void)hipDeviceSynchronize();
   (void)hipFree(te->cache);
+  (void)hipFree(te->cache_u);
   (void)hipFree(te->scratch);
   delete te;
   return PS_OK;
@@ -447,7 +451,7 @@ static ps_status te_row(ps_time_embed* te, float t, const std::vector<int>& pinn
   if (victim < 0) return fail(PS_ERR_INVALID_ARG, "time embed: more distinct timesteps in one batch than capacity");
   const int D = te->d.hidden;
   PS_HIP(launch_time_embed(t, te->d.wt1, te->d.bt1, te->d.wt2, te->d.bt2, te->d.wp, te->d.bp, D, te->scratch,
-                           te->cache + (size_t)victim * 6 * D, hs));
+                           te->cache + (size_t)victim * 6 * D, te->cache_u + (size_t)victim * D, hs));
   te->valid[victim] = 1;
   te->key[victim] = k;
   te->used[victim] = ++te->clock;
@@ -671,6 +675,113 @@ extern "C" ps_status ps_stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_em
   if (st) return st;
   for (int i = 0; i < n; ++i) p->ledger[writes[i]] = tasks[i].chunk;
   return PS_OK;
+}
+
+// ------------------------------------------------------------------- head
+struct ps_head {
+  ps_head_desc d{};
+  int device = 0;
+  DevBuf ws_x;     // compute-dtype copy of the latent patches (embedding's A operand)
+  DevBuf ws_y;     // modulated LN of h (head's A operand), row stride D + 64
+  DevBuf ws_mod;   // [n][6][D]: rows 0 and 1 = (shift, scale) of each task
+};
+
+extern "C" ps_status ps_head_create(const ps_head_desc* desc, ps_head** out) {
+  if (!desc || !out) return fail(PS_ERR_INVALID_ARG, "ps_head_create: null argument");
+  const ps_head_desc& d = *desc;
+  if (d.dtype != PS_BF16 && d.dtype != PS_F32) return fail(PS_ERR_INVALID_ARG, "ps_head_create: bad dtype");
+  const int step = gemm_k_step(d.dtype);
+  if (d.hidden <= 0 || d.latent_dim <= 0 || d.hidden % step != 0 || d.latent_dim % step != 0)
+    return fail(PS_ERR_INVALID_ARG, "ps_head_create: hidden %d and latent_dim %d must be positive multiples of %d",
+                d.hidden, d.latent_dim, step);
+  if (!d.w_embed || !d.w_head || !d.b_embed || !d.b_head || !d.t_head)
+    return fail(PS_ERR_INVALID_ARG, "ps_head_create: null weight pointer");
+  ps_head* h = new ps_head();
+  h->d = d;
+  (void)hipGetDevice(&h->device);
+  *out = h;
+  return PS_OK;
+}
+
+extern "C" ps_status ps_head_destroy(ps_head* h) {
+  if (!h) return fail(PS_ERR_INVALID_ARG, "ps_head_destroy: null handle");
+  (void)hipDeviceSynchronize();
+  h->ws_x.release();
+  h->ws_y.release();
+  h->ws_mod.release();
+  delete h;
+  return PS_OK;
+}
+
+static ps_status head_device_check(const ps_head* h, const char* fn) {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev != h->device) return fail(PS_ERR_INVALID_ARG, "%s: current device is not the head's", fn);
+  return PS_OK;
+}
+
+extern "C" ps_status ps_patch_embed(ps_head* h, const float* x, float* out, int32_t n_rows, hipStream_t hs) {
+  if (!h || !x || !out) return fail(PS_ERR_INVALID_ARG, "ps_patch_embed: null argument");
+  if (n_rows <= 0) return fail(PS_ERR_INVALID_ARG, "ps_patch_embed: n_rows %d must be positive", n_rows);
+  ps_status st = head_device_check(h, "ps_patch_embed");
+  if (st) return st;
+  const ps_head_desc& d = h->d;
+  const size_t n = (size_t)n_rows * d.latent_dim;
+  EpiArgs ep;
+  ep.bias = d.b_embed;
+  ep.out = out;
+  ep.ldo = d.hidden;
+  if (d.dtype == PS_BF16) {
+    if ((st = h->ws_x.reserve(n * sizeof(bf16)))) return st;
+    bf16* xb = static_cast<bf16*>(h->ws_x.p);
+    PS_HIP(launch_cast<bf16>(x, xb, n, hs));
+    PS_HIP(launch_gemm<bf16>(EPI_F32, xb, d.latent_dim, static_cast<const bf16*>(d.w_embed), n_rows, d.hidden,
+                             d.latent_dim, ep, nullptr, hs));
+  } else {
+    PS_HIP(launch_gemm<float>(EPI_F32, x, d.latent_dim, static_cast<const float*>(d.w_embed), n_rows, d.hidden,
+                              d.latent_dim, ep, nullptr, hs));
+  }
+  return PS_OK;
+}
+
+template <typename T>
+static ps_status run_head(ps_head* hd, const float* h, float* v, int M, int tokens, const float* mod, hipStream_t hs) {
+  const ps_head_desc& d = hd->d;
+  const int ldy = act_ld(d.hidden);
+  T* y = static_cast<T*>(hd->ws_y.p);
+  PS_HIP(launch_layernorm<T>(h, y, ldy, M, d.hidden, mod, 0, 1, tokens, hs));
+  EpiArgs ep;
+  ep.bias = d.b_head;
+  ep.out = v;
+  ep.ldo = d.latent_dim;
+  PS_HIP(launch_gemm<T>(EPI_F32, y, ldy, static_cast<const T*>(d.w_head), M, d.latent_dim, d.hidden, ep, nullptr, hs));
+  return PS_OK;
+}
+
+extern "C" ps_status ps_output_head(ps_head* hd, ps_time_embed* te, const float* t, int32_t n, int32_t tokens,
+                                    const float* h, float* v, hipStream_t hs) {
+  if (!hd || !te || !t || !h || !v) return fail(PS_ERR_INVALID_ARG, "ps_output_head: null argument");
+  if (n < 1 || n > PS_MAX_TASKS) return fail(PS_ERR_INVALID_ARG, "ps_output_head: n_tasks %d not in [1, %d]", n, PS_MAX_TASKS);
+  if (tokens <= 0) return fail(PS_ERR_INVALID_ARG, "ps_output_head: tokens %d must be positive", tokens);
+  ps_status st = head_device_check(hd, "ps_output_head");
+  if (st) return st;
+  const ps_head_desc& d = hd->d;
+  if (te->d.hidden != d.hidden) return fail(PS_ERR_INVALID_ARG, "ps_output_head: time embedding width differs");
+  for (int i = 0; i < n; ++i)
+    if (!isfinite(t[i])) return fail(PS_ERR_INVALID_ARG, "ps_output_head: t[%d] not finite", i);
+  const size_t M = (size_t)n * tokens;
+  if (M > (size_t)INT32_MAX / 2) return fail(PS_ERR_INVALID_ARG, "ps_output_head: too many rows");
+  if ((st = hd->ws_y.reserve(M * act_ld(d.hidden) * elt_size(d.dtype)))) return st;
+  if ((st = hd->ws_mod.reserve(sizeof(float) * (size_t)n * 6 * d.hidden))) return st;
+  std::vector<int> rows(n), pinned;
+  for (int i = 0; i < n; ++i) {
+    if ((st = te_row(te, t[i], pinned, hs, &rows[i]))) return st;
+    pinned.push_back(rows[i]);
+  }
+  float* mod = static_cast<float*>(hd->ws_mod.p);
+  PS_HIP(launch_head_mod(te->cache_u, rows.data(), d.t_head, mod, n, d.hidden, hs));
+  if (d.dtype == PS_BF16) return run_head<bf16>(hd, h, v, (int)M, tokens, mod, hs);
+  return run_head<float>(hd, h, v, (int)M, tokens, mod, hs);
 }
 
 // ------------------------------------------------------------------ euler

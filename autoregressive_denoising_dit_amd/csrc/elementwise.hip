@@ -341,14 +341,58 @@ hipError_t launch_put_tasks(const TaskTable& tt, DevTask* dst, hipStream_t s) {
 }
 
 hipError_t launch_time_embed(float t, const float* wt1, const float* bt1, const float* wt2, const float* bt2,
-                             const float* wp, const float* bp, int D, float* scratch, float* e, hipStream_t s) {
+                             const float* wp, const float* bp, int D, float* scratch, float* e, float* u,
+                             hipStream_t s) {
   float* phi = scratch;
   float* u1 = scratch + PS_FREQ_DIM;
-  float* u2 = u1 + D;
+  float* u2 = u;
   hipLaunchKernelGGL(k_sinusoid, dim3(1), dim3(128), 0, s, t, phi);
   hipLaunchKernelGGL(k_gemv, dim3((D + 3) / 4), dim3(256), 0, s, phi, PS_FREQ_DIM, wt1, bt1, u1, D, 0);
   hipLaunchKernelGGL(k_gemv, dim3((D + 3) / 4), dim3(256), 0, s, u1, D, wt2, bt2, u2, D, 1);
   hipLaunchKernelGGL(k_gemv, dim3((6 * D + 3) / 4), dim3(256), 0, s, u2, D, wp, bp, e, 6 * D, 1);
+  return hipGetLastError();
+}
+
+// y[i] = x[i] in the compute dtype (round to nearest even)
+template <typename T>
+__global__ void k_cast(const float* __restrict__ x, T* __restrict__ y, size_t n) {
+  const size_t i = (blockIdx.x * (size_t)blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  const f32x4 v = *reinterpret_cast<const f32x4*>(x + i);
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x4*>(y + i) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  } else {
+    *reinterpret_cast<f32x4*>(y + i) = v;
+  }
+}
+
+template <typename T>
+hipError_t launch_cast(const float* x, T* y, size_t n, hipStream_t s) {
+  if (n % 4 != 0) return hipErrorInvalidValue;
+  const size_t n4 = n / 4;
+  hipLaunchKernelGGL((k_cast<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, x, y, n);
+  return hipGetLastError();
+}
+template hipError_t launch_cast<bf16>(const float*, bf16*, size_t, hipStream_t);
+template hipError_t launch_cast<float>(const float*, float*, size_t, hipStream_t);
+
+// Output-head modulation: rows 0 (shift) and 1 (scale) of task i's [6][D]
+// block of mod = u(t_i) + t_head; the other four rows are not touched.
+__global__ void k_head_mod(const float* __restrict__ u_cache, Rows rows, const float* __restrict__ t_head,
+                           float* __restrict__ mod, int n_tasks, int D) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_tasks * 2 * D) return;
+  const int ti = idx / (2 * D), j = idx - ti * 2 * D;
+  mod[(size_t)ti * 6 * D + j] = u_cache[(size_t)rows.r[ti] * D + (j % D)] + t_head[j];
+}
+
+hipError_t launch_head_mod(const float* u_cache, const int* u_rows_host, const float* t_head, float* mod,
+                           int n_tasks, int D, hipStream_t s) {
+  if (n_tasks < 1 || n_tasks > PS_MAX_TASKS) return hipErrorInvalidValue;
+  Rows rows{};
+  for (int i = 0; i < n_tasks; ++i) rows.r[i] = u_rows_host[i];
+  const int n = n_tasks * 2 * D;
+  hipLaunchKernelGGL(k_head_mod, dim3((n + 255) / 256), dim3(256), 0, s, u_cache, rows, t_head, mod, n_tasks, D);
   return hipGetLastError();
 }
 

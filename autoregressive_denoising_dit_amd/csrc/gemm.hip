@@ -224,6 +224,10 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
     for (int r = rq; r < nrows; r += 4) {
       const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
       if (!col_ok) continue;
+      if constexpr (EPI == EPI_F32) {
+        store4(static_cast<float*>(ep.out) + (size_t)(rbase + r) * ep.ldo + col, v);
+        continue;
+      }
       f32x4 o;
       if constexpr (EPI == EPI_STORE) {
         o = v * ep.out_scale;
@@ -567,6 +571,7 @@ static hipError_t launch_gemm_mi(int epi, const T* A, int lda, const T* B, int M
     case EPI_STORE: hipLaunchKernelGGL((k_gemm<T, EPI_STORE, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
     case EPI_GELU: hipLaunchKernelGGL((k_gemm<T, EPI_GELU, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
     case EPI_RES: hipLaunchKernelGGL((k_gemm<T, EPI_RES, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
+    case EPI_F32: hipLaunchKernelGGL((k_gemm<T, EPI_F32, MI>), grid, block, 0, s, A, B, M, N, K, lda, e, tt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

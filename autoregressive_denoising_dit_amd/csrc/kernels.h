@@ -12,6 +12,7 @@ enum Epi {
   EPI_STORE = 2,   // (acc + bias) * out_scale -> out (compute dtype)
   EPI_GELU = 3,    // GELU_tanh(acc + bias) -> out (compute dtype)
   EPI_RES = 4,     // h_out = h_in + gate * (acc + bias), gate = mod[task][gate_row] or 1
+  EPI_F32 = 5,     // acc + bias -> out (fp32)
 };
 
 struct EpiArgs {
@@ -61,10 +62,19 @@ hipError_t launch_modulation(const float* e_cache, const int* e_rows_host, const
                              float* mod, float2* rope_f, const DevTask* tasks, int n_tasks, int D,
                              int frames, int seg_f, hipStream_t s);
 
-// Timestep embedding of one t into e (fp32 [6][D]) using scratch (>= 2 * D + 256 floats).
+// Timestep embedding of one t into e (fp32 [6][D]) and the timestep MLP
+// output u (fp32 [D]) using scratch (>= D + 256 floats).
 hipError_t launch_time_embed(float t, const float* wt1, const float* bt1, const float* wt2,
                              const float* bt2, const float* wp, const float* bp, int D, float* scratch,
-                             float* e, hipStream_t s);
+                             float* e, float* u, hipStream_t s);
+
+// y = x in the compute dtype (n a multiple of 4).
+template <typename T>
+hipError_t launch_cast(const float* x, T* y, size_t n, hipStream_t s);
+
+// Rows 0 and 1 of each task's [6][D] block of mod: u[u_rows[task]] + t_head.
+hipError_t launch_head_mod(const float* u_cache, const int* u_rows_host, const float* t_head, float* mod,
+                           int n_tasks, int D, hipStream_t s);
 
 // RoPE tables of one axis: tab[p][i] = (cos, sin)(p * 10000^(-2 i / seg)), p < n_pos.
 hipError_t launch_rope_table(float2* tab, int n_pos, int seg, hipStream_t s);

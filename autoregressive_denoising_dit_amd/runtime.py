@@ -192,6 +192,67 @@ class TimeEmbed:
             pass
 
 
+class Head:
+    """Patch embedding and output head on the device: w_embed [D, P] and w_head
+    [P, D] in the compute dtype ([out, in]); b_embed [D], b_head [P], t_head
+    [2, D] fp32.  The tensors are kept alive for as long as the handle."""
+
+    def __init__(self, tensors: Dict[str, torch.Tensor], hidden: int, latent_dim: int, dtype: int):
+        self.lib = _lib.load()
+        D, P = hidden, latent_dim
+        td = TORCH_DTYPE[dtype]
+        _need(tensors["w_embed"], td, (D, P), "w_embed")
+        _need(tensors["w_head"], td, (P, D), "w_head")
+        _need(tensors["b_embed"], torch.float32, (D,), "b_embed")
+        _need(tensors["b_head"], torch.float32, (P,), "b_head")
+        _need(tensors["t_head"], torch.float32, (2, D), "t_head")
+        self.tensors, self.hidden, self.latent_dim, self.dtype = tensors, D, P, dtype
+        d = _lib.HeadDesc(D, P, dtype, *[tensors[k].data_ptr()
+                                         for k in ("w_embed", "w_head", "b_embed", "b_head", "t_head")])
+        h = C.c_void_p()
+        check(self.lib.ps_head_create(C.byref(d), C.byref(h)))
+        self.handle = h
+
+    @classmethod
+    def from_numpy(cls, w: Dict[str, np.ndarray], hidden: int, latent_dim: int, dtype: int, device="cuda"):
+        """Uploads weights given as [in, out] arrays (y = x @ W + b)."""
+        td = TORCH_DTYPE[dtype]
+        t = {k: torch.from_numpy(np.ascontiguousarray(np.asarray(w[k], np.float32).T)).to(device, td).contiguous()
+             for k in ("w_embed", "w_head")}
+        for k in ("b_embed", "b_head", "t_head"):
+            t[k] = torch.from_numpy(np.ascontiguousarray(np.asarray(w[k], np.float32))).to(device)
+        return cls(t, hidden, latent_dim, dtype)
+
+    def close(self):
+        if self.handle:
+            check(self.lib.ps_head_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def patch_embed(head: Head, x: torch.Tensor, h: torch.Tensor, cuda_stream=None) -> None:
+    """h = x W_embed^T + b_embed for latent patches x [rows, P] (fp32) -> h [rows, D] (fp32)."""
+    rows = x.shape[0]
+    _need(x, torch.float32, (rows, head.latent_dim), "x")
+    _need(h, torch.float32, (rows, head.hidden), "h")
+    check(head.lib.ps_patch_embed(head.handle, _ptr(x), _ptr(h), rows, _stream_ptr(cuda_stream)))
+
+
+def output_head(head: Head, te: TimeEmbed, timesteps: Sequence[float], tokens: int, h: torch.Tensor,
+                v: torch.Tensor, cuda_stream=None) -> None:
+    """v = head(h) per task (tokens rows each, timestep timesteps[i]): h [n * tokens, D] -> v [n * tokens, P]."""
+    n = len(timesteps)
+    _need(h, torch.float32, (n * tokens, head.hidden), "h")
+    _need(v, torch.float32, (n * tokens, head.latent_dim), "v")
+    arr = (C.c_float * n)(*[float(t) for t in timesteps])
+    check(head.lib.ps_output_head(head.handle, te.handle, arr, n, tokens, _ptr(h), _ptr(v), _stream_ptr(cuda_stream)))
+
+
 def make_task(stream: int, chunk: int, step: int, timestep: float, write_slot: int,
               read_slots: Iterable[int]) -> Task:
     rs = list(read_slots)

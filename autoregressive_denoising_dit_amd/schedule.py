@@ -17,6 +17,11 @@ step updates them in place -- no gather or scatter copies.
 
 Ring slots: chunk c uses slot c mod R of its (stream, block, step), R >= W + k;
 it reads the slots of chunks max(0, c - W) .. c - 1 (fewer while c < W).
+
+With a patch embedding and output head (``runtime.Head``) the latents are a
+chunk's latent patches [L, P]: the tick's rows are embedded into the residual
+stream before block 0, and after the last block the head turns each task's
+rows into the velocity of its Euler step.
 """
 from __future__ import annotations
 
@@ -26,7 +31,7 @@ from typing import Callable, List, Optional, Sequence, Tuple
 import torch
 
 from . import runtime
-from .runtime import Block, Pool, TimeEmbed
+from .runtime import Block, Head, Pool, TimeEmbed
 
 
 def tick_tasks(tau: int, n_chunks: int, n_steps: int, k: int, n_streams: int) -> List[Tuple[int, int, int]]:
@@ -50,14 +55,19 @@ class StaggeredRunner:
     """Runs the staggered schedule of `n_chunks` chunks of `n_streams` streams."""
 
     def __init__(self, pool: Pool, blocks: Sequence[Block], te: TimeEmbed, timesteps: Sequence[float],
-                 window: int, k: int, n_streams: int):
+                 window: int, k: int, n_streams: int, head: Optional[Head] = None):
         if pool.n_slots < window + k:
             raise ValueError(f"ring of {pool.n_slots} slots is smaller than window + k = {window + k}")
-        self.pool, self.blocks, self.te = pool, list(blocks), te
+        if head is not None and head.hidden != pool.hidden:
+            raise ValueError("head width differs from the pool's")
+        self.pool, self.blocks, self.te, self.head = pool, list(blocks), te, head
         self.ts = list(timesteps) + [0.0]
         self.S, self.W, self.k, self.n_streams = len(timesteps), window, k, n_streams
         self.L, self.D = pool.tokens, pool.hidden
-        self.hbuf = torch.empty((self.S * k * n_streams * self.L, self.D), dtype=torch.float32, device="cuda")
+        self.P = head.latent_dim if head is not None else self.D   # latent values per token
+        rows = self.S * k * n_streams * self.L
+        self.hbuf = torch.empty((rows, self.D), dtype=torch.float32, device="cuda")
+        self.vbuf = torch.empty((rows, self.P), dtype=torch.float32, device="cuda") if head is not None else None
 
     def tasks_for(self, tau: int, n_chunks: int):
         tl = tick_tasks(tau, n_chunks, self.S, self.k, self.n_streams)
@@ -70,19 +80,27 @@ class StaggeredRunner:
         return tl, ps_tasks
 
     def run_tick(self, tau: int, x: torch.Tensor, n_chunks: int):
-        """x: fp32 [n_chunks, n_streams, L, D] latents (updated in place)."""
+        """x: fp32 [n_chunks, n_streams, L, P] latents (P = D without a head),
+        updated in place."""
         tl, tasks = self.tasks_for(tau, n_chunks)
         if not tl:
             return tl
         c_lo = tl[0][1]
         n = len(tl)
         rows = n * self.L
-        xs = x[c_lo:c_lo + n // self.n_streams].view(rows, self.D)
+        xs = x[c_lo:c_lo + n // self.n_streams].view(rows, self.P)
         h = self.hbuf[:rows]
+        if self.head is not None:
+            runtime.patch_embed(self.head, xs, h)
         for b, blk in enumerate(self.blocks):
-            runtime.stage_batch(self.pool, blk, self.te, tasks, xs if b == 0 else h, h)
+            runtime.stage_batch(self.pool, blk, self.te, tasks, xs if (b == 0 and self.head is None) else h, h)
         dts = [self.ts[s] - self.ts[s + 1] for (_, _, s) in tl]
-        runtime.euler_update(xs, h, dts, self.L, self.D)
+        if self.head is not None:
+            v = self.vbuf[:rows]
+            runtime.output_head(self.head, self.te, [self.ts[s] for (_, _, s) in tl], self.L, h, v)
+            runtime.euler_update(xs, v, dts, self.L, self.P)
+        else:
+            runtime.euler_update(xs, h, dts, self.L, self.D)
         return tl
 
     def run(self, x: torch.Tensor, n_chunks: int, on_tick: Optional[Callable[[int, list], None]] = None):

@@ -138,9 +138,9 @@ ps_status ps_block_destroy(ps_block* block);
  *   phi(t) = [cos(1000 t w_j) | sin(1000 t w_j)], w_j = 10000^(-j/128), j < 128
  *   u = SiLU(phi wt1^T + bt1) wt2^T + bt2;  e = SiLU(u) wp^T + bp.
  * Weights fp32, borrowed: wt1 [D, 256], bt1 [D], wt2 [D, D], bt2 [D],
- * wp [6D, D], bp [6D].  e(t) is computed once per distinct t (bitwise) and kept
- * in a cache of `capacity` rows; the least recently used row is replaced when
- * the cache is full. */
+ * wp [6D, D], bp [6D].  e(t) and u(t) are computed once per distinct t
+ * (bitwise) and kept in a cache of `capacity` rows; the least recently used
+ * row is replaced when the cache is full. */
 typedef struct {
   int32_t hidden;
   int32_t capacity;
@@ -193,6 +193,46 @@ typedef struct {
 ps_status ps_stage_batch(ps_kv_pool* pool, const ps_block* block, ps_time_embed* te,
                          const ps_task* tasks, int32_t n_tasks, const float* h_in,
                          float* h_out, hipStream_t hs);
+
+/* ------------------------------------------------------------------ head --
+ * The steps either side of the block stack (a Wan-style reading; the pages
+ * evaluate Wan-family backbones -- AREX article on the PhysisServe report,
+ * section "实测数字" -- whose latent frame of 60 x 104 in 2 x 2 patches is a
+ * chunk's 30 x 52 token grid).  A chunk's latent is carried patchified:
+ * x [tokens, P] fp32, P = latent channels x patch volume, a token's values
+ * ordered (channel, frame, row, col) inside its patch.
+ *   patch embedding: h0 = x w_embed^T + b_embed (a 3D convolution whose kernel
+ *   and stride are the patch, written as a linear map);
+ *   output head: (shift, scale) = u(t) + t_head, u(t) the timestep MLP output
+ *   (see the timestep embedding); v = (LN(h)(1 + scale) + shift) w_head^T + b_head.
+ * Weights borrowed until ps_head_destroy: w_embed [D, P] and w_head [P, D]
+ * in the compute dtype ([out, in]); b_embed [D], b_head [P], t_head [2, D]
+ * fp32.  Requirements: D and P multiples of 64 (bf16) or 32 (fp32). */
+typedef struct {
+  int32_t hidden;      /* D */
+  int32_t latent_dim;  /* P */
+  ps_dtype dtype;
+  const void *w_embed, *w_head;
+  const float *b_embed, *b_head, *t_head;
+} ps_head_desc;
+
+typedef struct ps_head ps_head;
+
+ps_status ps_head_create(const ps_head_desc* desc, ps_head** out);
+ps_status ps_head_destroy(ps_head* head);
+
+/* h0 of n_rows tokens: x device fp32 [n_rows, P] -> h device fp32 [n_rows, D].
+ * The library's workspace for the compute-dtype copy of x grows on demand
+ * (PS_ERR_OUT_OF_MEMORY if it cannot). */
+ps_status ps_patch_embed(ps_head* head, const float* x, float* h, int32_t n_rows, hipStream_t hs);
+
+/* v of a batch of tasks: task i (rows i*tokens .. i*tokens+tokens-1 of h)
+ * uses timestep t[i] (host fp32 [n_tasks]); h device fp32 [n_tasks * tokens,
+ * D] -> v device fp32 [n_tasks * tokens, P].  te: the shared timestep
+ * embedding, whose cache also keeps u(t).  Errors as ps_patch_embed, and
+ * PS_ERR_INVALID_ARG if te's width is not D or a t[i] is not finite. */
+ps_status ps_output_head(ps_head* head, ps_time_embed* te, const float* t, int32_t n_tasks,
+                         int32_t tokens, const float* h, float* v, hipStream_t hs);
 
 /* ----------------------------------------------------------------- euler --
  * Flow-matching Euler step after the last block: for task i,

@@ -3,12 +3,14 @@
 Bar: max |err| / RMS(ref) <= 3e-2 with bf16 operands and <= 1e-4 with fp32
 operands, on every tensor compared (stage output, its branch delta and the
 cache entries written)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from autoregressive_denoising_dit_amd import runtime
+from autoregressive_denoising_dit_amd import _lib, runtime
 from autoregressive_denoising_dit_amd._lib import PsError, PS_ERR_SLOT_CONFLICT, PS_ERR_INVALID_ARG
 from synthetic import C1, C2, C3, C4, C5, inputs, with_
 from tests.gpu_util import (StageCase, host, make_block, make_pool, make_te, rel_err, say, to_dev, tol)
@@ -250,6 +252,87 @@ def test_schedule_batch_invariance_bitwise_c3_shape():
     b = _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, 1, 1)
     assert np.array_equal(a, b)
     assert np.all(np.isfinite(a))
+
+
+# ------------------------------------------------- patch embedding / head
+@pytest.mark.parametrize("cfg", [C1, C3, C4], ids=lambda c: c.name)
+def test_patch_embed_and_output_head(cfg):
+    """Both steps either side of the block stack on one batch of tasks at
+    different timesteps (the head's modulation differs per task)."""
+    n = 3 if cfg is C1 else 2
+    L, P, D = cfg.tokens, cfg.latent_dim, cfg.hidden
+    hw = inputs.head_weights(cfg, 0)
+    tw = inputs.time_weights(cfg, 0)
+    x = np.concatenate([inputs.latent_patches(cfg, 0, c, 0) for c in range(n)])
+    h = inputs.hidden_rows(cfg, n, 0, tag="head_h")
+    ts = [cfg.timesteps[i % cfg.n_steps] for i in range(n)][::-1]
+    say("head", cfg.name, "tasks", n, "timesteps", ts)
+    td = runtime.ps_dtype(cfg.dtype)
+    head = runtime.Head.from_numpy(hw, D, P, td)
+    te = make_te(cfg, tw)
+    xg = to_dev(x, torch.float32)
+    h0 = torch.empty((n * L, D), dtype=torch.float32, device="cuda")
+    runtime.patch_embed(head, xg, h0)
+    v = torch.empty((n * L, P), dtype=torch.float32, device="cuda")
+    runtime.output_head(head, te, ts, L, to_dev(h, torch.float32), v)
+    torch.cuda.synchronize()
+    e0 = rel_err(host(h0), oracle.patch_embed(x, hw))
+    say(f"patch embed err {e0:.2e}")
+    assert e0 <= tol(cfg)
+    for i in range(n):
+        ref = oracle.output_head(h[i * L:(i + 1) * L], oracle.time_mlp(ts[i], tw), hw)
+        e = rel_err(host(v[i * L:(i + 1) * L]), ref)
+        say(f"head task {i} (t = {ts[i]}) err {e:.2e}")
+        assert e <= tol(cfg)
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_schedule_c1_with_head_matches_oracle(k):
+    """The tiny configuration end to end on latent patches: patch embedding,
+    2 blocks x 2 steps, output head and Euler per tick (staggered on the GPU,
+    sequential in the oracle)."""
+    from autoregressive_denoising_dit_amd.schedule import StaggeredRunner
+    cfg, n_chunks = C1, 4
+    blocks, tw, ctxs, _ = _schedule_inputs(cfg, n_chunks, 1)
+    hw = inputs.head_weights(cfg, 0)
+    lat = {c: inputs.latent_patches(cfg, 0, c, 0) for c in range(n_chunks)}
+    say("schedule c1 with head", k)
+    pool = make_pool(cfg, n_streams=1, n_blocks=cfg.n_blocks, n_slots=cfg.window + k)
+    blks = [make_block(cfg, w, b) for b, w in enumerate(blocks)]
+    te = make_te(cfg, tw)
+    for blk in blks:
+        pool.context_set(blk, 0, to_dev(ctxs[0], torch.float32))
+    head = runtime.Head.from_numpy(hw, cfg.hidden, cfg.latent_dim, runtime.ps_dtype(cfg.dtype))
+    x = torch.stack([to_dev(lat[c], torch.float32)[None] for c in range(n_chunks)]).contiguous()
+    StaggeredRunner(pool, blks, te, cfg.timesteps, cfg.window, k, 1, head=head).run(x, n_chunks)
+    torch.cuda.synchronize()
+    gx = host(x)
+    ox, _ = oracle.run_schedule(cfg, blocks, tw, lambda sg, c: lat[c], ctxs, n_chunks, order="sequential",
+                                head=hw)
+    for c in range(n_chunks):
+        e = rel_err(gx[c, 0], ox[(0, c)])
+        say(f"chunk {c}: x^S err {e:.2e}")
+        assert e <= 1e-4
+
+
+def test_head_rejects_bad_arguments():
+    cfg = C3
+    hw = {k: to_dev(v.T if v.ndim == 2 and k.startswith("w") else v,
+                    torch.bfloat16 if k.startswith("w") else torch.float32)
+          for k, v in inputs.head_weights(cfg, 0).items()}
+    with pytest.raises(ValueError):
+        runtime.Head(hw, cfg.hidden, cfg.latent_dim + 1, runtime.PS_BF16)
+    bad = _lib.HeadDesc(cfg.hidden, 40, runtime.PS_BF16, *[hw[k].data_ptr() for k in
+                                                          ("w_embed", "w_head", "b_embed", "b_head", "t_head")])
+    h = ctypes.c_void_p()
+    st = _lib.load().ps_head_create(ctypes.byref(bad), ctypes.byref(h))
+    assert st == _lib.PS_ERR_INVALID_ARG
+    head = runtime.Head(hw, cfg.hidden, cfg.latent_dim, runtime.PS_BF16)
+    te = make_te(cfg, inputs.time_weights(cfg, 0))
+    hh = torch.zeros((cfg.tokens, cfg.hidden), dtype=torch.float32, device="cuda")
+    v = torch.zeros((cfg.tokens, cfg.latent_dim), dtype=torch.float32, device="cuda")
+    with pytest.raises(_lib.PsError):
+        runtime.output_head(head, te, [float("nan")], cfg.tokens, hh, v)
 
 
 # ------------------------------------------------------------ error paths
