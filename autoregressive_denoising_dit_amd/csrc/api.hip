@@ -734,12 +734,12 @@ extern "C" ps_status ps_patch_embed(ps_head* h, const float* x, float* out, int3
   if (d.dtype == PS_BF16) {
     if ((st = h->ws_x.reserve(n * sizeof(bf16)))) return st;
     bf16* xb = static_cast<bf16*>(h->ws_x.p);
-    PS_HIP(launch_cast<bf16>(x, xb, n, hs));
-    PS_HIP(launch_gemm<bf16>(EPI_F32, xb, d.latent_dim, static_cast<const bf16*>(d.w_embed), n_rows, d.hidden,
-                             d.latent_dim, ep, nullptr, hs));
+    PS_TRACED("embed_cast", launch_cast<bf16>(x, xb, n, hs));
+    PS_TRACED("embed", (launch_gemm<bf16>(EPI_F32, xb, d.latent_dim, static_cast<const bf16*>(d.w_embed), n_rows,
+                                          d.hidden, d.latent_dim, ep, nullptr, hs)));
   } else {
-    PS_HIP(launch_gemm<float>(EPI_F32, x, d.latent_dim, static_cast<const float*>(d.w_embed), n_rows, d.hidden,
-                              d.latent_dim, ep, nullptr, hs));
+    PS_TRACED("embed", (launch_gemm<float>(EPI_F32, x, d.latent_dim, static_cast<const float*>(d.w_embed), n_rows,
+                                           d.hidden, d.latent_dim, ep, nullptr, hs)));
   }
   return PS_OK;
 }
@@ -749,12 +749,13 @@ static ps_status run_head(ps_head* hd, const float* h, float* v, int M, int toke
   const ps_head_desc& d = hd->d;
   const int ldy = act_ld(d.hidden);
   T* y = static_cast<T*>(hd->ws_y.p);
-  PS_HIP(launch_layernorm<T>(h, y, ldy, M, d.hidden, mod, 0, 1, tokens, hs));
+  PS_TRACED("head_ln", (launch_layernorm<T>(h, y, ldy, M, d.hidden, mod, 0, 1, tokens, hs)));
   EpiArgs ep;
   ep.bias = d.b_head;
   ep.out = v;
   ep.ldo = d.latent_dim;
-  PS_HIP(launch_gemm<T>(EPI_F32, y, ldy, static_cast<const T*>(d.w_head), M, d.latent_dim, d.hidden, ep, nullptr, hs));
+  PS_TRACED("head_gemm",
+            (launch_gemm<T>(EPI_F32, y, ldy, static_cast<const T*>(d.w_head), M, d.latent_dim, d.hidden, ep, nullptr, hs)));
   return PS_OK;
 }
 
@@ -779,7 +780,7 @@ extern "C" ps_status ps_output_head(ps_head* hd, ps_time_embed* te, const float*
     pinned.push_back(rows[i]);
   }
   float* mod = static_cast<float*>(hd->ws_mod.p);
-  PS_HIP(launch_head_mod(te->cache_u, rows.data(), d.t_head, mod, n, d.hidden, hs));
+  PS_TRACED("head_mod", launch_head_mod(te->cache_u, rows.data(), d.t_head, mod, n, d.hidden, hs));
   if (d.dtype == PS_BF16) return run_head<bf16>(hd, h, v, (int)M, tokens, mod, hs);
   return run_head<float>(hd, h, v, (int)M, tokens, mod, hs);
 }

@@ -34,6 +34,16 @@ from . import runtime
 from .runtime import Block, Head, Pool, TimeEmbed
 
 
+def shifted_timesteps(n_steps: int, shift: float = 1.0) -> Tuple[float, ...]:
+    """Timesteps t_0 > ... > t_{S-1} (t_S = 0): the uniform grid u = 1 - s/S
+    under the flow-matching time shift t = a u / (1 + (a - 1) u), a = shift.
+    a = 1 is the uniform schedule; a > 1 spends more of the steps at high
+    noise.  The pages fix four steps but no values."""
+    if n_steps < 1 or not shift > 0:
+        raise ValueError("need n_steps >= 1 and shift > 0")
+    return tuple(shift * (1.0 - s / n_steps) / (1.0 + (shift - 1.0) * (1.0 - s / n_steps)) for s in range(n_steps))
+
+
 def tick_tasks(tau: int, n_chunks: int, n_steps: int, k: int, n_streams: int) -> List[Tuple[int, int, int]]:
     """(stream, chunk, step) of tick tau, ordered by chunk then stream."""
     out = []

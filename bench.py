@@ -94,12 +94,14 @@ def setup_stage(cfg, n_tasks, seed=0):
     return dict(pool=pool, blk=blk, te=te, x=x, h=h, xe=xe, w=w, tw=tw)
 
 
-def run_stagger_bench(cfg, measured=64):
+def run_stagger_bench(cfg, measured=64, with_head=False):
     """Steady-state chunk interval of one stream under the staggered schedule
     (all blocks, all steps, k chunks per step per tick): `measured` chunks
     completed after a warm-up of S + W + 2 ticks, from events recorded after
     each tick's Euler step.  As many further ticks then run with per-kernel
-    events, for the time per tick of each kernel."""
+    events, for the time per tick of each kernel.  With `with_head` the
+    latents are latent patches [L, P]: the patch embedding runs before block 0
+    and the output head after the last block of every tick."""
     import torch
     from autoregressive_denoising_dit_amd import runtime
     from autoregressive_denoising_dit_amd.schedule import StaggeredRunner
@@ -125,12 +127,17 @@ def run_stagger_bench(cfg, measured=64):
         keep.append(w)
     tw = {"wt1": rn(D, 256), "bt1": rn(D), "wt2": rn(D, D), "bt2": rn(D), "wp": rn(6 * D, D), "bp": rn(6 * D)}
     te = runtime.TimeEmbed(tw, D, capacity=16)
-    runner = StaggeredRunner(pool, blocks, te, cfg.timesteps, W, k, 1)
+    head = None
+    if with_head:
+        P = cfg.latent_dim
+        head = runtime.Head({"w_embed": rn(D, P, dtype=td), "w_head": rn(P, D, dtype=td), "b_embed": rn(D),
+                             "b_head": rn(P), "t_head": rn(2, D)}, D, P, runtime.ps_dtype(cfg.dtype))
+    runner = StaggeredRunner(pool, blocks, te, cfg.timesteps, W, k, 1, head=head)
     tau0 = S + W + 2                       # warm-up ticks (pipeline filled, full windows)
     tau1 = tau0 + (measured + k - 1) // k  # each later tick completes k chunks
     tau2 = tau1 + (tau1 - tau0)            # then as many ticks again with per-kernel events
     n_chunks = k * (tau2 + 1)
-    x = rn(n_chunks, 1, cfg.tokens, D, std=1.0)
+    x = rn(n_chunks, 1, cfg.tokens, cfg.latent_dim if with_head else D, std=1.0)
     from autoregressive_denoising_dit_amd import _lib
     torch.cuda.synchronize()
     ev = {}
@@ -348,6 +355,8 @@ def main():
     ap.add_argument("--workload", default="c5", choices=["c2", "c5", "c3", "c4"],
                     help="c5 (default) / c2: one stage batch per step; c3 / c4: the staggered schedule "
                          "over all blocks and steps, reporting the chunk interval")
+    ap.add_argument("--head", action="store_true",
+                    help="c3 / c4: run on latent patches with the patch embedding and output head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
@@ -371,14 +380,15 @@ def main():
         return
     if args.workload in ("c3", "c4"):
         cfg = get(args.workload)
-        interval, tick, done, per_tick = run_stagger_bench(cfg)
+        interval, tick, done, per_tick = run_stagger_bench(cfg, with_head=args.head)
         per_chunk = cfg.n_blocks * cfg.n_steps * stage_flops(cfg, cfg.window)
         print(json.dumps({
             "metric": "steady-state chunk interval (ms), staggered schedule, one stream",
             "value": round(interval, 3), "unit": "ms", "n_gpus": 1, "higher_is_better": False,
             "dtype": cfg.dtype, "data": "synthetic (seeded random-init weights, N(0,1) latents and contexts)",
             "config": {"workload": cfg.name, "blocks": cfg.n_blocks, "steps": cfg.n_steps, "k": cfg.k,
-                       "window": cfg.window, "tokens_per_chunk": cfg.tokens, "hidden": cfg.hidden},
+                       "window": cfg.window, "tokens_per_chunk": cfg.tokens, "hidden": cfg.hidden,
+                       "head": bool(args.head), "latent_dim": cfg.latent_dim if args.head else None},
             "chunks_measured": done, "tick_ms": round(tick, 3),
             "stage_tasks_per_s": round(cfg.n_blocks * cfg.n_steps * cfg.k / (tick * 1e-3), 1),
             "mfma_frac": round(per_chunk / (interval * 1e-3) / PEAK[cfg.dtype], 4),

@@ -22,4 +22,4 @@ from .block import (  # noqa: F401
     token_positions,
 )
 from .head import output_head, patch_embed, patchify, time_mlp, unpatchify  # noqa: F401
-from .schedule import RingPool, run_schedule, staggered_ticks  # noqa: F401
+from .schedule import RingPool, run_schedule, shifted_timesteps, staggered_ticks  # noqa: F401

@@ -34,6 +34,21 @@ from .block import F64, context_kv, modulation, qkv_phase, rest_phase, time_embe
 from .head import output_head, patch_embed, time_mlp
 
 
+def shifted_timesteps(n_steps: int, shift: float = 1.0) -> tuple:
+    """t_0 > ... > t_{S-1} of an S-step sampler: the uniform grid u_s = 1 - s/S
+    warped by the flow-matching time shift t = a u / (1 + (a - 1) u), a = shift
+    (a = 1 keeps the grid uniform; a > 1 spends more steps at high noise).
+    The pages give four steps and no values; the warp is the reading taken for
+    a non-uniform schedule.  t_S = 0 is implied."""
+    if n_steps < 1 or not shift > 0:
+        raise ValueError("need n_steps >= 1 and shift > 0")
+    out = []
+    for s in range(n_steps):
+        u = 1.0 - s / n_steps
+        out.append(shift * u / (1.0 + (shift - 1.0) * u))
+    return tuple(out)
+
+
 class SlotConflict(RuntimeError):
     pass
 

@@ -115,3 +115,13 @@ def test_tick_tasks_match_oracle_definition():
         ref = oracle.staggered_ticks(9, 4, k, 2)
         for tau, tasks in enumerate(ref):
             assert sorted(tick_tasks(tau, 9, 4, k, 2)) == sorted(tasks)
+
+
+@pytest.mark.parametrize("S,shift", [(4, 1.0), (4, 3.0), (7, 5.0), (1, 2.0)])
+def test_shifted_timesteps_match_the_oracle(S, shift):
+    import oracle
+    from autoregressive_denoising_dit_amd.schedule import shifted_timesteps
+    got, ref = shifted_timesteps(S, shift), oracle.shifted_timesteps(S, shift)
+    assert len(got) == S
+    for a, b in zip(got, ref):
+        assert a == pytest.approx(b, rel=1e-15, abs=0)

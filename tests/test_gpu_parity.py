@@ -315,6 +315,35 @@ def test_schedule_c1_with_head_matches_oracle(k):
         assert e <= 1e-4
 
 
+def test_schedule_c1_shifted_timesteps_matches_oracle():
+    """The tiny configuration end to end with a non-uniform (shift 3) schedule
+    of three steps, on latent patches with the head."""
+    from autoregressive_denoising_dit_amd.schedule import StaggeredRunner, shifted_timesteps
+    ts = shifted_timesteps(3, 3.0)
+    cfg, n_chunks, k = with_(C1, timesteps=ts), 4, 1
+    blocks, tw, ctxs, _ = _schedule_inputs(cfg, n_chunks, 1)
+    hw = inputs.head_weights(cfg, 0)
+    lat = {c: inputs.latent_patches(cfg, 0, c, 0) for c in range(n_chunks)}
+    say("schedule c1 shifted timesteps", ts)
+    pool = make_pool(cfg, n_streams=1, n_blocks=cfg.n_blocks, n_slots=cfg.window + k)
+    blks = [make_block(cfg, w, b) for b, w in enumerate(blocks)]
+    te = make_te(cfg, tw)
+    for blk in blks:
+        pool.context_set(blk, 0, to_dev(ctxs[0], torch.float32))
+    head = runtime.Head.from_numpy(hw, cfg.hidden, cfg.latent_dim, runtime.ps_dtype(cfg.dtype))
+    x = torch.stack([to_dev(lat[c], torch.float32)[None] for c in range(n_chunks)]).contiguous()
+    StaggeredRunner(pool, blks, te, ts, cfg.window, k, 1, head=head).run(x, n_chunks)
+    torch.cuda.synchronize()
+    gx = host(x)
+    ocfg = with_(cfg, timesteps=oracle.shifted_timesteps(3, 3.0))
+    ox, _ = oracle.run_schedule(ocfg, blocks, tw, lambda sg, c: lat[c], ctxs, n_chunks, order="sequential",
+                                head=hw)
+    for c in range(n_chunks):
+        e = rel_err(gx[c, 0], ox[(0, c)])
+        say(f"chunk {c}: x^S err {e:.2e}")
+        assert e <= 1e-4
+
+
 def test_head_rejects_bad_arguments():
     cfg = C3
     hw = {k: to_dev(v.T if v.ndim == 2 and k.startswith("w") else v,

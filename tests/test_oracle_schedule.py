@@ -182,3 +182,33 @@ def test_staggered_ticks_cover_each_task_once(k):
     # steady state: k tasks per step per stream
     mid = ticks[S + 1]
     assert len(mid) == 2 * S * k
+
+
+# --- non-uniform timestep schedules -------------------------------------------
+def test_shifted_timesteps_special_cases():
+    # shift 1 is the uniform grid the configs use
+    assert oracle.shifted_timesteps(4, 1.0) == pytest.approx((1.0, 0.75, 0.5, 0.25), abs=0)
+    # hand values: shift 3 maps u = 0.5 to 1.5 / 2 = 0.75 and u = 0.25 to 0.75 / 1.5 = 0.5
+    t = oracle.shifted_timesteps(4, 3.0)
+    assert t[0] == 1.0 and t[2] == pytest.approx(0.75, rel=1e-15) and t[3] == pytest.approx(0.5, rel=1e-15)
+    assert oracle.shifted_timesteps(1, 5.0) == (1.0,)
+
+
+@pytest.mark.parametrize("shift", [0.5, 1.0, 3.0, 5.0])
+def test_shifted_timesteps_invert_to_the_uniform_grid(shift):
+    S = 7
+    t = np.array(oracle.shifted_timesteps(S, shift))
+    assert np.all(np.diff(t) < 0) and t[0] == 1.0 and t[-1] > 0
+    # the warp's inverse u = t / (a - (a - 1) t) recovers 1 - s/S
+    u = t / (shift - (shift - 1.0) * t)
+    np.testing.assert_allclose(u, 1.0 - np.arange(S) / S, rtol=1e-14)
+    # a > 1 keeps every step at or above the uniform one (more time at high noise)
+    if shift > 1:
+        assert np.all(t >= 1.0 - np.arange(S) / S)
+
+
+def test_shifted_timesteps_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.shifted_timesteps(0, 1.0)
+    with pytest.raises(ValueError):
+        oracle.shifted_timesteps(4, 0.0)
