@@ -33,6 +33,8 @@ EXPORTS = (
     "ps_time_embed_destroy", "ps_time_embed_get", "ps_context_set", "ps_stage_batch",
     "ps_euler_update", "ps_last_error", "ps_trace_enable", "ps_trace_collect", "ps_trace_count",
     "ps_trace_entry", "ps_head_create", "ps_head_destroy", "ps_patch_embed", "ps_output_head",
+    "ps_sched_create", "ps_sched_destroy", "ps_sched_split", "ps_sched_admit", "ps_sched_release",
+    "ps_sched_gpu",
 )
 
 
@@ -62,6 +64,12 @@ class TimeDesc(C.Structure):
 class HeadDesc(C.Structure):
     _fields_ = ([("hidden", C.c_int32), ("latent_dim", C.c_int32), ("dtype", C.c_int32)]
                 + [(n, C.c_void_p) for n in ("w_embed", "w_head", "b_embed", "b_head", "t_head")])
+
+
+class SchedDesc(C.Structure):
+    _fields_ = [("n_gpus", C.c_int32), ("positions", C.c_int32), ("n_blocks", C.c_int32), ("n_steps", C.c_int32),
+                ("max_discrepancy", C.c_int32), ("reserved", C.c_int32), ("slo_ms", C.c_double),
+                ("batch_fixed_ms", C.c_double), ("batch_task_ms", C.c_double)]
 
 
 class Task(C.Structure):
@@ -102,6 +110,12 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ps_head_destroy": [vp],
         "ps_patch_embed": [vp, vp, vp, i32, vp],
         "ps_output_head": [vp, vp, C.POINTER(C.c_float), i32, i32, vp, vp, vp],
+        "ps_sched_create": [C.POINTER(SchedDesc), C.POINTER(vp)],
+        "ps_sched_destroy": [vp],
+        "ps_sched_split": [vp, C.POINTER(i32)],
+        "ps_sched_admit": [vp, C.c_int64, C.POINTER(i32), i32, C.POINTER(i32)],
+        "ps_sched_release": [vp, C.c_int64, C.POINTER(i32)],
+        "ps_sched_gpu": [vp, i32, C.POINTER(i32), C.POINTER(C.c_double)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -28,6 +28,15 @@ ps_status fail(ps_status st, const char* fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+// error reporting for the host-only parts of the library (placement)
+namespace ps {
+ps_status set_error(ps_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace ps
+
+namespace {
+
 #define PS_HIP(call)                                                                 \
   do {                                                                               \
     hipError_t e_ = (call);                                                          \

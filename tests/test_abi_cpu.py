@@ -13,13 +13,14 @@ from autoregressive_denoising_dit_amd import _lib
 from autoregressive_denoising_dit_amd.schedule import n_ticks, tick_tasks
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ps.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 needs_lib = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libps.so not built")
 
 
 def header_functions():
-    txt = open(HEADER).read()
+    txt = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:ps_status|const char\*|int32_t)\s+(ps_\w+)\s*\(", txt, re.M)))
 
 
@@ -39,10 +40,13 @@ def test_struct_layout_matches_ctypes(tmp_path):
 #include <stdio.h>
 #include <stddef.h>
 #include "ps.h"
+#include "ps_sched.h"
 int main(void) {
   printf("%zu %zu %zu %zu\n", sizeof(ps_pool_desc), sizeof(ps_block_desc), sizeof(ps_time_desc), sizeof(ps_task));
   printf("%zu %zu %zu %zu\n", offsetof(ps_block_desc, wqkv), offsetof(ps_block_desc, tmod),
          offsetof(ps_time_desc, wt1), offsetof(ps_task, read_slots));
+  printf("%zu %zu %zu %zu\n", sizeof(ps_head_desc), offsetof(ps_head_desc, w_embed), sizeof(ps_sched_desc),
+         offsetof(ps_sched_desc, slo_ms));
   return 0;
 }
 ''')
@@ -55,7 +59,8 @@ int main(void) {
     got = [int(x) for x in out]
     want = [C.sizeof(_lib.PoolDesc), C.sizeof(_lib.BlockDesc), C.sizeof(_lib.TimeDesc), C.sizeof(_lib.Task),
             _lib.BlockDesc.wqkv.offset, _lib.BlockDesc.tmod.offset, _lib.TimeDesc.wt1.offset,
-            _lib.Task.read_slots.offset]
+            _lib.Task.read_slots.offset, C.sizeof(_lib.HeadDesc), _lib.HeadDesc.w_embed.offset,
+            C.sizeof(_lib.SchedDesc), _lib.SchedDesc.slo_ms.offset]
     assert got == want
 
 
