@@ -68,7 +68,7 @@ class HeadDesc(C.Structure):
 
 class SchedDesc(C.Structure):
     _fields_ = [("n_gpus", C.c_int32), ("positions", C.c_int32), ("n_blocks", C.c_int32), ("n_steps", C.c_int32),
-                ("max_discrepancy", C.c_int32), ("reserved", C.c_int32), ("slo_ms", C.c_double),
+                ("max_discrepancy", C.c_int32), ("ranks_per_stream", C.c_int32), ("slo_ms", C.c_double),
                 ("batch_fixed_ms", C.c_double), ("batch_task_ms", C.c_double)]
 
 

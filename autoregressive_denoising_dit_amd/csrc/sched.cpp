@@ -65,17 +65,21 @@ struct ps_sched {
     for (auto& bt : r.blocks) g.tasks[bt.first] += sign * bt.second;
   }
 
-  // the fewest contiguous stage groups that each meet the SLO alone
+  // contiguous stage groups that each meet the SLO alone: the fewest, or
+  // exactly d.ranks_per_stream of them
   void split() {
     const int B = d.n_blocks, N = d.n_blocks * d.n_steps;
     Gpu empty;
     empty.tasks.assign(B, 0);
-    for (int R = 1; R <= N; ++R) {
+    const int r_lo = d.ranks_per_stream ? d.ranks_per_stream : 1;
+    const int r_hi = d.ranks_per_stream ? d.ranks_per_stream : N;
+    for (int R = r_lo; R <= r_hi && R <= N; ++R) {
       std::vector<Rank> groups(R);
       bool ok = true;
       for (int r = 0; r < R && ok; ++r) {
         std::vector<int> cnt(B, 0);
-        for (int p = (int)((int64_t)r * N / R); p < (int)((int64_t)(r + 1) * N / R); ++p) ++cnt[p % B];
+        // stages in block-major order: stage p is block p / n_steps
+        for (int p = (int)((int64_t)r * N / R); p < (int)((int64_t)(r + 1) * N / R); ++p) ++cnt[p / d.n_steps];
         for (int b = 0; b < B; ++b)
           if (cnt[b]) groups[r].blocks.emplace_back(b, cnt[b]);
         ok = cycle_with(empty, groups[r]) <= d.slo_ms;
@@ -127,7 +131,7 @@ extern "C" ps_status ps_sched_create(const ps_sched_desc* desc, ps_sched** out) 
   const ps_sched_desc& d = *desc;
   if (d.n_gpus < 1 || d.positions < 1 || d.n_blocks < 1 || d.n_steps < 1 || d.max_discrepancy < 0 ||
       (int64_t)d.n_blocks * d.n_steps > (1 << 16) || !(d.slo_ms > 0) || !(d.batch_fixed_ms >= 0) ||
-      !(d.batch_task_ms > 0) || d.reserved != 0)
+      !(d.batch_task_ms > 0) || d.ranks_per_stream < 0)
     return ps::set_error(PS_ERR_INVALID_ARG, "ps_sched_create: field out of range");
   ps_sched* s = new (std::nothrow) ps_sched;
   if (!s) return ps::set_error(PS_ERR_OUT_OF_MEMORY, "ps_sched_create: out of host memory");

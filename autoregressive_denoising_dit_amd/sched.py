@@ -19,10 +19,10 @@ from .runtime import check
 
 class Scheduler:
     def __init__(self, n_gpus: int, positions: int, n_blocks: int, n_steps: int, slo_ms: float,
-                 batch_fixed_ms: float, batch_task_ms: float, max_discrepancy: int = 2):
+                 batch_fixed_ms: float, batch_task_ms: float, max_discrepancy: int = 2, ranks_per_stream: int = 0):
         self.lib = _lib.load()
-        d = _lib.SchedDesc(n_gpus, positions, n_blocks, n_steps, max_discrepancy, 0, slo_ms, batch_fixed_ms,
-                           batch_task_ms)
+        d = _lib.SchedDesc(n_gpus, positions, n_blocks, n_steps, max_discrepancy, ranks_per_stream, slo_ms,
+                           batch_fixed_ms, batch_task_ms)
         h = C.c_void_p()
         check(self.lib.ps_sched_create(C.byref(d), C.byref(h)))
         self.handle, self.n_gpus = h, n_gpus

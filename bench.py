@@ -160,6 +160,64 @@ def run_stagger_bench(cfg, measured=64, with_head=False):
     return interval, tick, done, per_tick
 
 
+def run_batch_sweep(cfg, sizes=(1, 2, 4, 8, 16), steps=20, warmup=4):
+    """Time of one block batch (ps_stage_batch, full windows, steps mixed) for
+    each batch size n; least-squares fit t(n) = a + b n."""
+    import numpy as np
+    import torch
+    from autoregressive_denoising_dit_amd import runtime
+    out = {}
+    for n in sizes:
+        _log(f"batch sweep {cfg.name}: {n} tasks")
+        st = setup_stage(cfg, n)
+        tls = [stage_tasks(cfg, n, tau) for tau in range(cfg.n_steps)]
+        for tau in range(warmup):
+            runtime.stage_batch(st["pool"], st["blk"], st["te"], tls[tau % cfg.n_steps], st["x"], st["h"])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for tau in range(steps):
+            runtime.stage_batch(st["pool"], st["blk"], st["te"], tls[tau % cfg.n_steps], st["x"], st["h"])
+        e1.record()
+        torch.cuda.synchronize()
+        out[n] = e0.elapsed_time(e1) / steps
+        del st
+        torch.cuda.empty_cache()
+    ns = np.array(sorted(out), dtype=np.float64)
+    ts = np.array([out[n] for n in sorted(out)])
+    b, a = np.polyfit(ns, ts, 1)
+    return out, float(a), float(b)
+
+
+def run_placement(cfg, a, b, n_gpus=24, max_discrepancy=2):
+    """Streams of one model admitted on a pool of GPUs by the joint placement
+    against an equal split (each stream its own group of GPUs), for several
+    chunk-interval SLOs, with the measured batch cost a + b n."""
+    from autoregressive_denoising_dit_amd.sched import Scheduler, admitted_streams
+    # one memory position per virtual rank: HBM left after weights over the KV
+    # rings of the largest rank (ring slots of L tokens x 2D per stage, bf16)
+    slot_bytes = cfg.tokens * 2 * cfg.hidden * 2
+    rows = []
+    stages = cfg.n_blocks * cfg.n_steps
+    alone_one_gpu = cfg.n_blocks * (a + b * cfg.n_steps)      # whole stream on one GPU
+    for frac in (0.7, 0.4, 0.3, 0.15, 0.08):
+        slo = alone_one_gpu * frac * 1.0001
+        probe = Scheduler(n_gpus, 1 << 20, cfg.n_blocks, cfg.n_steps, slo, a, b, max_discrepancy)
+        R = probe.split()
+        if R == 0:
+            continue
+        row = {"slo_ms": round(slo, 2), "ranks_per_stream": R, "equal_split_streams": n_gpus // R}
+        # joint placement with the fewest ranks, and with four times finer ranks
+        # (one discrepancy: the search over many small ranks grows quickly)
+        for key, nr, disc in (("joint_streams", 0, max_discrepancy), ("joint_streams_fine", min(stages, 4 * R), 1)):
+            per_rank = -(-stages // (nr or R)) * (cfg.window + 1) * slot_bytes
+            positions = max(1, int(200e9 // per_rank))
+            row[key] = admitted_streams(Scheduler(n_gpus, positions, cfg.n_blocks, cfg.n_steps, slo, a, b, disc, nr))
+            row[key.replace("streams", "ranks")] = nr or R
+        rows.append(row)
+    return rows
+
+
 def stage_tasks(cfg, n_tasks, tau, base_chunk=100):
     """Task i: stream i at step (tau + i) mod S, a steady-state chunk with a full window."""
     from autoregressive_denoising_dit_amd import runtime
@@ -352,9 +410,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c5", "c3", "c4"],
+    ap.add_argument("--workload", default="c5", choices=["c2", "c5", "c3", "c4", "placement"],
                     help="c5 (default) / c2: one stage batch per step; c3 / c4: the staggered schedule "
-                         "over all blocks and steps, reporting the chunk interval")
+                         "over all blocks and steps, reporting the chunk interval; placement: block-batch "
+                         "cost sweep at the 1.3B and 5B shapes and the joint placement it drives")
     ap.add_argument("--head", action="store_true",
                     help="c3 / c4: run on latent patches with the patch embedding and output head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -377,6 +436,17 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "placement":
+        res = {}
+        for name in ("c3", "c4"):
+            cfg = get(name)
+            times, a, b = run_batch_sweep(cfg)
+            res[cfg.name] = {"batch_ms": {str(n): round(t, 3) for n, t in times.items()},
+                             "fit_ms": {"fixed": round(a, 4), "per_task": round(b, 4)},
+                             "placement_24_gpus": run_placement(cfg, a, b)}
+        print(json.dumps({"metric": "streams admitted on 24 GPUs, joint placement vs equal split",
+                          "n_gpus": 1, "data": "synthetic; batch costs measured on this GPU", **res}), flush=True)
         return
     if args.workload in ("c3", "c4"):
         cfg = get(args.workload)

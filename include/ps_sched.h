@@ -13,10 +13,12 @@
  * "时分复用" and "虚拟 rank 的动态放置", Fig. 3 and Fig. 4).
  *
  * The model (readings where the pages are silent):
- *  - stages are (block b, step s) in pipeline order p = s * n_blocks + b; a
- *    stream of R virtual ranks takes the contiguous groups of stages
- *    [floor(r N / R), floor((r + 1) N / R)), N = n_blocks * n_steps, and R is
- *    the smallest count whose every group alone on a GPU meets the SLO;
+ *  - stages are (block b, step s) in block-major order p = b * n_steps + s, so
+ *    that a rank holds whole blocks where it can and their steps batch
+ *    together; a stream of R virtual ranks takes the groups of stages
+ *    [floor(r N / R), floor((r + 1) N / R)), N = n_blocks * n_steps; R is the
+ *    smallest count whose every group alone on a GPU meets the SLO, or a fixed
+ *    count (finer ranks can fill capacity the fewest would leave);
  *  - a GPU's cycle (the chunk interval it sustains) is the sum over blocks, in
  *    block order, of f(n_b) = batch_fixed_ms + batch_task_ms * n_b for the
  *    n_b > 0 hosted tasks of block b;
@@ -46,7 +48,7 @@ typedef struct ps_sched_desc {
   int32_t n_blocks;          /* Transformer blocks of the model, >= 1 */
   int32_t n_steps;           /* denoising steps, >= 1; n_blocks * n_steps <= 1 << 16 */
   int32_t max_discrepancy;   /* LDS limit, >= 0 */
-  int32_t reserved;          /* 0 */
+  int32_t ranks_per_stream;  /* 0: the fewest that meet the SLO alone; else exactly this many (<= stages) */
   double slo_ms;             /* chunk-interval target, > 0 */
   double batch_fixed_ms;     /* per-batch cost a, >= 0 */
   double batch_task_ms;      /* per-task cost b, > 0 */
@@ -59,8 +61,8 @@ typedef struct ps_sched ps_sched;
 ps_status ps_sched_create(const ps_sched_desc* desc, ps_sched** out);
 ps_status ps_sched_destroy(ps_sched* s);
 
-/* Virtual ranks a stream needs to meet the SLO alone (*n_ranks = 0 if no
- * split does). */
+/* Virtual ranks of a stream (*n_ranks = 0 if the split cannot meet the SLO
+ * alone: then every stream is rejected). */
 ps_status ps_sched_split(const ps_sched* s, int32_t* n_ranks);
 
 /* Tries to admit stream `stream` (an id not currently admitted).  On

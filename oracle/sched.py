@@ -13,9 +13,11 @@ layer 3; 163.com release, section "PhysisServe", bullets "时分复用" and
     placed and it meets its SLO running alone; running streams never move.
 
 Readings where the pages are silent (each one a plain choice):
-  * stages are (block b, step s) in pipeline order p = s * B + b; a stream of R
-    virtual ranks takes the contiguous groups [floor(r N / R), floor((r+1) N / R));
-    R is the smallest count whose every group, alone on a GPU, meets the SLO;
+  * stages are (block b, step s) in block-major order p = b * S + s, so that a
+    rank holds whole blocks where it can and their steps batch together (as
+    one GPU serving one block's four stages); a stream of R virtual ranks takes
+    the groups [floor(r N / R), floor((r+1) N / R)); R is the smallest count
+    whose every group, alone on a GPU, meets the SLO, or a fixed count;
   * a GPU's cycle -- the time to run every hosted task once, which is the
     chunk interval it sustains -- is sum over blocks of f(n_b), with n_b the
     hosted tasks on block b and f(n) = a + b n for n > 0, f(0) = 0 (one batch
@@ -56,6 +58,7 @@ class Cluster:
     positions: int         # M: virtual ranks per GPU
     slo_ms: float          # T
     model: Model
+    n_ranks: int = 0       # virtual ranks per stream (0: the fewest that meet the SLO)
     # per GPU: list of (stream, rank index, {block: task count})
     hosted: List[List[Tuple[int, int, Dict[int, int]]]] = field(default_factory=list)
 
@@ -84,13 +87,16 @@ def cycle_ms(model: Model, ranks: Sequence[Dict[int, int]]) -> float:
     return c
 
 
-def split_stream(model: Model, slo_ms: float) -> Optional[List[Dict[int, int]]]:
-    """The stream's virtual ranks: the fewest contiguous groups of stages in
-    pipeline order each of which meets the SLO alone; None if no count does."""
+def split_stream(model: Model, slo_ms: float, n_ranks: int = 0) -> Optional[List[Dict[int, int]]]:
+    """The stream's virtual ranks: contiguous groups of stages in pipeline
+    order, each of which must meet the SLO alone -- the fewest such groups
+    (n_ranks = 0) or exactly n_ranks of them; None if that is impossible."""
     B, S = model.n_blocks, model.n_steps
     N = B * S
-    stages = [(p % B, p // B) for p in range(N)]
-    for R in range(1, N + 1):
+    stages = [(p // S, p % S) for p in range(N)]     # block-major: all steps of block 0, then block 1, ...
+    for R in ([n_ranks] if n_ranks else range(1, N + 1)):
+        if R > N:
+            return None
         groups = [block_counts(stages[(r * N) // R:((r + 1) * N) // R]) for r in range(R)]
         if all(cycle_ms(model, [g]) <= slo_ms for g in groups):
             return groups
@@ -147,7 +153,7 @@ def admit(cl: Cluster, stream: int, max_disc: int) -> Optional[List[int]]:
     """Admits `stream` if it meets the SLO alone and all its virtual ranks can
     be placed; running streams stay where they are.  Returns the GPUs of its
     ranks, or None (cluster unchanged)."""
-    ranks = split_stream(cl.model, cl.slo_ms)
+    ranks = split_stream(cl.model, cl.slo_ms, cl.n_ranks)
     if ranks is None:
         return None
     place = lds_place(cl, ranks, max_disc)
@@ -193,6 +199,7 @@ def exists_placement(cl: Cluster, ranks: Sequence[Dict[int, int]]) -> bool:
 
 def equal_split_streams(n_gpus: int, model: Model, slo_ms: float) -> int:
     """Streams served when each gets its own group of GPUs, one virtual rank
-    per GPU (no sharing, no cross-stream batching): floor(G / R)."""
+    per GPU (no sharing, no cross-stream batching): floor(G / R), R the fewest
+    ranks that meet the SLO."""
     ranks = split_stream(model, slo_ms)
     return 0 if ranks is None else n_gpus // len(ranks)

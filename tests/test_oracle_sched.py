@@ -24,13 +24,14 @@ def test_cycle_hand_values():
 
 def test_split_stream_hand_values():
     m = S.Model(4, 2, 1.0, 1.0)          # f(n) = 1 + n; 8 stages, a stage alone costs 2
-    # R = 1: blocks 0..3 twice -> 4 * 3 = 12; R = 2: 4 distinct blocks -> 8; R = 3: sizes 2, 3, 3 -> 4, 6, 6
+    # block-major order (b0 s0, b0 s1, b1 s0, ...).  R = 1: 4 blocks x f(2) = 12;
+    # R = 2: blocks {0, 1} and {2, 3}, 2 x f(2) = 6; R = 3: sizes 2, 3, 3 ->
+    # {b0: 2} = 3, {b1: 2, b2: 1} = 5, {b2: 1, b3: 2} = 5
     assert len(S.split_stream(m, 12.0)) == 1
-    assert len(S.split_stream(m, 11.9)) == 2
-    g = S.split_stream(m, 7.0)
-    assert g == [{0: 1, 1: 1}, {2: 1, 3: 1, 0: 1}, {1: 1, 2: 1, 3: 1}]
+    assert S.split_stream(m, 11.9) == [{0: 2, 1: 2}, {2: 2, 3: 2}]
+    assert S.split_stream(m, 5.9) == [{0: 2}, {1: 2, 2: 1}, {2: 1, 3: 2}]
     assert S.split_stream(m, 1.9) is None
-    assert S.equal_split_streams(24, m, 7.0) == 8
+    assert S.equal_split_streams(24, m, 5.9) == 8
 
 
 def test_best_fit_fails_one_discrepancy_succeeds():
@@ -76,7 +77,7 @@ def test_lds_is_complete_at_full_discrepancy_against_brute_force():
 
 def test_admission_whole_stream_and_no_migration():
     m = S.Model(4, 2, 1.0, 1.0)
-    cl = S.Cluster(3, 2, 7.0, m)            # a stream = 3 ranks (see the split test)
+    cl = S.Cluster(3, 2, 5.9, m)            # a stream = 3 ranks (see the split test)
     placed = {}
     sid = 0
     while True:
@@ -98,16 +99,32 @@ def test_admission_whole_stream_and_no_migration():
 
 
 def test_joint_placement_beats_equal_split_when_batching_pays():
-    # f(n) = 2 + n / 4: two stages of one block cost 2.5, of two blocks 4.5.
-    # SLO 6: a stream splits into 4 ranks of 2 stages (4.5 each), so an equal
-    # split serves one stream on 4 GPUs; shared GPUs batch the same blocks
-    # across streams and hold all four.
+    # f(n) = 2 + n / 4: a block's two steps cost 2.5 as one batch.  SLO 6: a
+    # stream splits into 2 ranks of 2 blocks (5 each), so an equal split
+    # serves 2 streams on 4 GPUs; a GPU holding the same 2 blocks of two
+    # streams batches them (2 x (2 + 1) = 6) and the pool holds 4 streams.
     m = S.Model(4, 2, 2.0, 0.25)
     slo = 6.0
     g = S.split_stream(m, slo)
-    assert len(g) == 4 and all(S.cycle_ms(m, [x]) == 4.5 for x in g)
+    assert g == [{0: 2, 1: 2}, {2: 2, 3: 2}] and all(S.cycle_ms(m, [x]) == 5.0 for x in g)
     cl = S.Cluster(4, 8, slo, m)
     n = 0
     while S.admit(cl, n, 2) is not None:
         n += 1
-    assert S.equal_split_streams(4, m, slo) == 1 and n == 4
+    assert S.equal_split_streams(4, m, slo) == 2 and n == 4
+
+
+def test_fixed_rank_count_split():
+    m = S.Model(4, 2, 1.0, 1.0)
+    assert S.split_stream(m, 7.0, 4) == [{0: 2}, {1: 2}, {2: 2}, {3: 2}]
+    assert S.split_stream(m, 5.9, 2) is None           # two blocks x f(2) = 6 > 5.9
+    assert S.split_stream(m, 7.0, 9) is None           # more ranks than stages
+    # finer ranks fill capacity the fewest leave: SLO 9 on 3 GPUs.  Fewest
+    # ranks: 2 of 6 -> one stream per pair of GPUs (a GPU cannot take two).
+    # 4 ranks of one block (3 each): a GPU holds blocks {b, b'} of one stream
+    # (6) or one block of two streams (1 + 4 = 5) plus another of one (8).
+    cl = S.Cluster(3, 16, 9.0, m, n_ranks=4)
+    n = 0
+    while S.admit(cl, n, 1) is not None:
+        n += 1
+    assert S.equal_split_streams(3, m, 9.0) == 1 and n == 2

@@ -12,10 +12,10 @@ from oracle import sched as S
 needs_lib = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libps.so not built")
 
 
-def _pair(n_gpus, positions, B, St, slo, a, b, disc):
+def _pair(n_gpus, positions, B, St, slo, a, b, disc, n_ranks=0):
     from autoregressive_denoising_dit_amd.sched import Scheduler
-    nat = Scheduler(n_gpus, positions, B, St, slo, a, b, disc)
-    ora = S.Cluster(n_gpus, positions, slo, S.Model(B, St, a, b))
+    nat = Scheduler(n_gpus, positions, B, St, slo, a, b, disc, n_ranks)
+    ora = S.Cluster(n_gpus, positions, slo, S.Model(B, St, a, b), n_ranks=n_ranks)
     return nat, ora
 
 
@@ -27,8 +27,9 @@ def test_admission_sequences_match_oracle(seed):
     a, b = rng.choice([(0.0, 1.0), (0.5, 0.25), (1.0, 0.3), (0.074, 0.227)])
     slo = rng.choice([2.0, 3.0, 4.5, 7.0, 12.0])
     n_gpus, positions, disc = rng.choice([2, 3, 5, 8]), rng.choice([1, 2, 4, 8]), rng.choice([0, 1, 2])
-    nat, ora = _pair(n_gpus, positions, B, St, slo, a, b, disc)
-    ranks = S.split_stream(ora.model, slo)
+    n_ranks = rng.choice([0, 0, 1, 3, B])
+    nat, ora = _pair(n_gpus, positions, B, St, slo, a, b, disc, n_ranks)
+    ranks = S.split_stream(ora.model, slo, n_ranks)
     assert nat.split() == (0 if ranks is None else len(ranks))
     live = []
     for step in range(40):
