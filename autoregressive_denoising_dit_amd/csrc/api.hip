@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <cstdarg>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -184,7 +185,33 @@ struct ps_kv_pool {
   int64_t slot_elems = 0, ctx_elems = 0;
   std::vector<int> ctx_len;   // per (stream, block); 0 = context not set
   std::vector<int> ledger;    // per (region, slot): chunk id, -1 = empty
-  DevBuf ws_mod, ws_rope, ws_y, ws_q, ws_a, ws_u, ws_tasks;
+  // Workspace of the calls on one HIP stream.  Batches submitted on
+  // different streams get different workspaces, so they may run
+  // concurrently (the caller keeps their KV slots apart).
+  struct Workspace {
+    hipStream_t stream = nullptr;
+    DevBuf mod, rope, y, q, a, u, tasks;
+    void release() {
+      mod.release();
+      rope.release();
+      y.release();
+      q.release();
+      a.release();
+      u.release();
+      tasks.release();
+    }
+  };
+  std::vector<Workspace*> ws;
+  Workspace* workspace(hipStream_t s) {
+    for (Workspace* w : ws)
+      if (w->stream == s) return w;
+    if ((int)ws.size() >= PS_MAX_STREAMS_PER_POOL) return nullptr;
+    Workspace* w = new (std::nothrow) Workspace;
+    if (!w) return nullptr;
+    w->stream = s;
+    ws.push_back(w);
+    return w;
+  }
   int L() const { return desc.frames * desc.rows * desc.cols; }
   int D() const { return desc.n_heads * desc.head_dim; }
   PoolGeo geo() const {
@@ -295,13 +322,11 @@ extern "C" ps_status ps_kv_pool_destroy(ps_kv_pool* p) {
   (void)hipFree(p->ctx);
   (void)hipFree(p->rope_y);
   (void)hipFree(p->rope_x);
-  p->ws_mod.release();
-  p->ws_rope.release();
-  p->ws_y.release();
-  p->ws_q.release();
-  p->ws_a.release();
-  p->ws_u.release();
-  p->ws_tasks.release();
+  for (auto* w : p->ws) {
+    w->release();
+    delete w;
+  }
+  p->ws.clear();
   delete p;
   return PS_OK;
 }
@@ -459,8 +484,14 @@ static ps_status te_row(ps_time_embed* te, float t, const std::vector<int>& pinn
   }
   if (victim < 0) return fail(PS_ERR_INVALID_ARG, "time embed: more distinct timesteps in one batch than capacity");
   const int D = te->d.hidden;
+  // A fill is rare (a new timestep).  It waits for all in-flight work, which
+  // may still read the victim row or use the scratch from another stream, and
+  // completes before the call returns, so that calls on any stream may read
+  // the row afterwards.
+  PS_HIP(hipDeviceSynchronize());
   PS_HIP(launch_time_embed(t, te->d.wt1, te->d.bt1, te->d.wt2, te->d.bt2, te->d.wp, te->d.bp, D, te->scratch,
                            te->cache + (size_t)victim * 6 * D, te->cache_u + (size_t)victim * D, hs));
+  PS_HIP(hipStreamSynchronize(hs));
   te->valid[victim] = 1;
   te->key[victim] = k;
   te->used[victim] = ++te->clock;
@@ -516,14 +547,14 @@ extern "C" ps_status ps_context_set(ps_kv_pool* p, const ps_block* b, int32_t st
 static int act_ld(int cols) { return cols + 64; }
 
 template <typename T>
-static ps_status run_stage(ps_kv_pool* p, const ps_block* b, const DevTask* tt, int n, const float* mod,
-                           const float2* rope_f, const float* h_in, float* h_out, hipStream_t hs) {
+static ps_status run_stage(ps_kv_pool* p, ps_kv_pool::Workspace* w, const ps_block* b, const DevTask* tt, int n,
+                           const float* mod, const float2* rope_f, const float* h_in, float* h_out, hipStream_t hs) {
   const ps_block_desc& bd = b->d;
   const int L = p->L(), D = bd.hidden, F = bd.ffn, M = n * L;
-  T* y = static_cast<T*>(p->ws_y.p);
-  T* q = static_cast<T*>(p->ws_q.p);
-  T* a = static_cast<T*>(p->ws_a.p);
-  T* u = static_cast<T*>(p->ws_u.p);
+  T* y = static_cast<T*>(w->y.p);
+  T* q = static_cast<T*>(w->q.p);
+  T* a = static_cast<T*>(w->a.p);
+  T* u = static_cast<T*>(w->u.p);
   const PoolGeo pg = p->geo();
   const float qscale = 1.4426950408889634f / sqrtf((float)bd.head_dim);
   const T* W = nullptr;
@@ -657,13 +688,16 @@ extern "C" ps_status ps_stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_em
   const int L = p->L(), D = bd.hidden, F = bd.ffn;
   const size_t M = (size_t)n * L, es = elt_size(bd.dtype);
   ps_status st;
-  if ((st = p->ws_mod.reserve(sizeof(float) * n * 6 * (size_t)D))) return st;
-  if ((st = p->ws_rope.reserve(sizeof(float2) * n * pd.frames * (size_t)(p->seg_f / 2) + 16))) return st;
-  if ((st = p->ws_y.reserve(M * act_ld(D) * es))) return st;
-  if ((st = p->ws_q.reserve(M * D * es))) return st;
-  if ((st = p->ws_a.reserve(M * act_ld(D) * es))) return st;
-  if ((st = p->ws_u.reserve(M * act_ld(F) * es))) return st;
-  if ((st = p->ws_tasks.reserve(sizeof(DevTask) * PS_MAX_TASKS))) return st;
+  ps_kv_pool::Workspace* w = p->workspace(hs);
+  if (!w)
+    return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: more than %d streams use this pool", PS_MAX_STREAMS_PER_POOL);
+  if ((st = w->mod.reserve(sizeof(float) * n * 6 * (size_t)D))) return st;
+  if ((st = w->rope.reserve(sizeof(float2) * n * pd.frames * (size_t)(p->seg_f / 2) + 16))) return st;
+  if ((st = w->y.reserve(M * act_ld(D) * es))) return st;
+  if ((st = w->q.reserve(M * D * es))) return st;
+  if ((st = w->a.reserve(M * act_ld(D) * es))) return st;
+  if ((st = w->u.reserve(M * act_ld(F) * es))) return st;
+  if ((st = w->tasks.reserve(sizeof(DevTask) * PS_MAX_TASKS))) return st;
 
   // timestep embeddings (cached per distinct t)
   std::vector<int> rows(n), pinned;
@@ -671,16 +705,16 @@ extern "C" ps_status ps_stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_em
     if ((st = te_row(te, tasks[i].timestep, pinned, hs, &rows[i]))) return st;
     pinned.push_back(rows[i]);
   }
-  float* mod = static_cast<float*>(p->ws_mod.p);
-  float2* rope_f = static_cast<float2*>(p->ws_rope.p);
-  DevTask* dtasks = static_cast<DevTask*>(p->ws_tasks.p);
+  float* mod = static_cast<float*>(w->mod.p);
+  float2* rope_f = static_cast<float2*>(w->rope.p);
+  DevTask* dtasks = static_cast<DevTask*>(w->tasks.p);
   PS_TRACED("put_tasks", launch_put_tasks(tt, dtasks, hs));
   PS_TRACED("modulation", launch_modulation(te->cache, rows.data(), bd.tmod, mod, rope_f, dtasks, n, D, pd.frames, p->seg_f, hs));
 
   if (bd.dtype == PS_BF16)
-    st = run_stage<bf16>(p, b, dtasks, n, mod, rope_f, h_in, h_out, hs);
+    st = run_stage<bf16>(p, w, b, dtasks, n, mod, rope_f, h_in, h_out, hs);
   else
-    st = run_stage<float>(p, b, dtasks, n, mod, rope_f, h_in, h_out, hs);
+    st = run_stage<float>(p, w, b, dtasks, n, mod, rope_f, h_in, h_out, hs);
   if (st) return st;
   for (int i = 0; i < n; ++i) p->ledger[writes[i]] = tasks[i].chunk;
   return PS_OK;

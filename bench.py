@@ -231,41 +231,71 @@ def stage_tasks(cfg, n_tasks, tau, base_chunk=100):
     return out
 
 
-def run_stage_bench(cfg, n_tasks, steps, warmup):
+def run_stage_bench(cfg, n_tasks, steps, warmup, overlap=1):
+    """Stage batches plus their Euler updates, `steps` timed after `warmup`.
+    With overlap = k > 1, step tau runs on stream tau mod k with its own output
+    and latent buffers: consecutive batches of the schedule touch different
+    (stream, step) regions of the pool, so they may overlap on the device."""
     import torch
     from autoregressive_denoising_dit_amd import _lib, runtime
-    _log(f"setting up {cfg.name}: {n_tasks} tasks per batch")
+    _log(f"setting up {cfg.name}: {n_tasks} tasks per batch, {overlap} stream(s)")
     st = setup_stage(cfg, n_tasks)
     L, D = cfg.tokens, cfg.hidden
     task_lists = [stage_tasks(cfg, n_tasks, tau) for tau in range(cfg.n_steps)]
     dts = [[cfg.timesteps[t.step] - (cfg.timesteps[t.step + 1] if t.step + 1 < cfg.n_steps else 0.0)
             for t in tl] for tl in task_lists]
+    main = torch.cuda.current_stream()
+    streams = [main] + [torch.cuda.Stream() for _ in range(overlap - 1)]
+    hs = [st["h"]] + [torch.empty_like(st["h"]) for _ in range(overlap - 1)]
+    xes = [st["xe"]] + [st["xe"].clone() for _ in range(overlap - 1)]
 
     def step(tau):
+        k = tau % overlap
         tl = task_lists[tau % cfg.n_steps]
-        runtime.stage_batch(st["pool"], st["blk"], st["te"], tl, st["x"], st["h"])
-        runtime.euler_update(st["xe"], st["h"], dts[tau % cfg.n_steps], L, D)
+        runtime.stage_batch(st["pool"], st["blk"], st["te"], tl, st["x"], hs[k], cuda_stream=streams[k])
+        runtime.euler_update(xes[k], hs[k], dts[tau % cfg.n_steps], L, D, cuda_stream=streams[k])
+
+    def fork(ev):
+        for s_ in streams[1:]:
+            s_.wait_event(ev)
+
+    def join():
+        for s_ in streams[1:]:
+            e = torch.cuda.Event()
+            e.record(s_)
+            main.wait_event(e)
 
     for tau in range(warmup):
         step(tau)
+    join()
     # timed region: no per-kernel events (they add a gap between kernels)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record()
+    ev[0].record(main)
+    fork(ev[0])
     for tau in range(steps):
         step(tau)
-        ev[tau + 1].record()
+        if overlap == 1:
+            ev[tau + 1].record(main)
+    if overlap > 1:
+        join()
+        ev[steps].record(main)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    assert torch.isfinite(st["h"]).all().item(), "non-finite stage output"
+    for h_ in hs:
+        assert torch.isfinite(h_).all().item(), "non-finite stage output"
     sec = (t1 - t0) / steps
-    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    if overlap == 1:
+        per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    else:
+        per_step = [ev[0].elapsed_time(ev[steps]) / steps] * steps
     # the same steps again with a HIP event pair around every kernel, recorded
     # by the library on the stream the kernel runs on: per-kernel durations
     _lib.trace_enable(True)
     for tau in range(steps):
         step(tau)
+    join()
     torch.cuda.synchronize()
     trace = _lib.trace_read()
     _lib.trace_enable(False)
@@ -414,6 +444,8 @@ def main():
                     help="c5 (default) / c2: one stage batch per step; c3 / c4: the staggered schedule "
                          "over all blocks and steps, reporting the chunk interval; placement: block-batch "
                          "cost sweep at the 1.3B and 5B shapes and the joint placement it drives")
+    ap.add_argument("--overlap", type=int, default=1,
+                    help="c5 / c2: streams that consecutive stage batches alternate over (1 = one stream)")
     ap.add_argument("--head", action="store_true",
                     help="c3 / c4: run on latent patches with the patch embedding and output head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -468,7 +500,7 @@ def main():
     cfg = get(args.workload)
     n_tasks = cfg.batch
     n_read = cfg.window
-    sec, trace, per_step = run_stage_bench(cfg, n_tasks, args.steps, args.warmup)
+    sec, trace, per_step = run_stage_bench(cfg, n_tasks, args.steps, args.warmup, args.overlap)
     sclk = shader_clock_mhz()
     flops_step = n_tasks * stage_flops(cfg, n_read)
     peak = PEAK[cfg.dtype]
@@ -510,7 +542,8 @@ def main():
         "data": "synthetic (seeded random-init weights, N(0,1) latents, contexts and pre-filled noisy KV)",
         "config": {"workload": cfg.name, "tasks_per_batch": n_tasks, "tokens_per_chunk": cfg.tokens,
                    "hidden": cfg.hidden, "heads": cfg.heads, "head_dim": cfg.head_dim, "ffn": cfg.ffn,
-                   "window": cfg.window, "ctx_tokens": cfg.n_ctx, "steps_mixed": cfg.n_steps},
+                   "window": cfg.window, "ctx_tokens": cfg.n_ctx, "steps_mixed": cfg.n_steps,
+                   "overlap_streams": args.overlap},
         # each stream's chunk needs one task per denoising step at this block
         "chunk_interval_ms": round(sec * 1e3 * cfg.n_steps, 3),
         "mfma_frac": round(flops_step / sec / peak, 4),

@@ -23,8 +23,13 @@
  *    "host" pointers are read before the call returns.  The caller owns every
  *    tensor pointer it passes; the library owns handles, the KV pool, the
  *    cached timestep embeddings and the internal workspace.
- *  - Handles are not thread-safe.  One handle is used from one host thread, and
- *    the calls that share a handle must be ordered on one stream.
+ *  - Handles are not thread-safe: one handle is used from one host thread.
+ *    ps_stage_batch calls on up to PS_MAX_STREAMS_PER_POOL different streams
+ *    may run concurrently on the device (each stream has its own workspace in
+ *    the pool), provided no batch reads or writes a KV slot that a concurrent
+ *    batch writes; all other calls that share a handle are ordered on one
+ *    stream.  Filling a timestep-embedding cache row (a timestep not cached)
+ *    waits for all device work and completes before the call returns.
  *  - Element types: ps_dtype PS_BF16 (bfloat16) or PS_F32.  "compute dtype"
  *    means the dtype of the pool/block.  The residual stream (h) and the
  *    latents (x) are always fp32; biases, modulation tables and the timestep
@@ -54,6 +59,7 @@ typedef int32_t ps_dtype;
 
 #define PS_MAX_WINDOW 8   /* most prior chunks one task may read */
 #define PS_MAX_TASKS 32   /* most tasks in one ps_stage_batch call */
+#define PS_MAX_STREAMS_PER_POOL 4   /* streams whose ps_stage_batch calls may overlap */
 #define PS_FREQ_DIM 256   /* sinusoidal timestep features */
 
 typedef struct ps_kv_pool ps_kv_pool;

@@ -344,6 +344,66 @@ def test_schedule_c1_shifted_timesteps_matches_oracle():
         assert e <= 1e-4
 
 
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_concurrent_batches_on_two_streams_match_sequential(name):
+    """Two stage batches of disjoint pool regions, submitted on two HIP streams
+    without synchronisation between them, give bitwise the outputs and cache
+    entries of the same batches run one after the other on one stream."""
+    cfg = {"c1": C1, "c2": C2}[name]
+    W = cfg.window
+    R = W + 1
+    w = inputs.block_weights(cfg, 0, 0)
+    tw = inputs.time_weights(cfg, 0)
+    td = runtime.TORCH_DTYPE[runtime.ps_dtype(cfg.dtype)]
+    n_per = 2 if name == "c1" else 1
+    say("concurrent batches", name)
+
+    def run(concurrent):
+        pool = make_pool(cfg, n_streams=2 * n_per, n_blocks=1, n_slots=R, check_slots=False)
+        blk = make_block(cfg, w, 0)
+        te = make_te(cfg, tw)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(5)
+        shape = (cfg.tokens, cfg.heads, cfg.head_dim)
+        for sg in range(2 * n_per):
+            pool.context_set(blk, sg, (torch.randn(cfg.n_ctx, cfg.hidden, generator=g, device="cuda", dtype=torch.float32)).to(td))
+            for st_ in range(cfg.n_steps):
+                for slot in range(R):
+                    pool.load(sg, 0, st_, slot, 0, torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32).to(td),
+                              torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32).to(td))
+        # batch A: streams 0..n_per-1; batch B: streams n_per..2 n_per-1; different steps
+        c = W + 2
+        mk = lambda sg, s: runtime.make_task(sg, c, s, cfg.timesteps[s], c % R, [(c - W + j) % R for j in range(W)])
+        ta = [mk(sg, 0) for sg in range(n_per)]
+        tb = [mk(n_per + sg, cfg.n_steps - 1) for sg in range(n_per)]
+        xa = torch.randn(n_per * cfg.tokens, cfg.hidden, generator=g, device="cuda", dtype=torch.float32)
+        xb = torch.randn(n_per * cfg.tokens, cfg.hidden, generator=g, device="cuda", dtype=torch.float32)
+        ha, hb = torch.empty_like(xa), torch.empty_like(xb)
+        # cache both timesteps first (a cache fill waits for the device)
+        runtime.stage_batch(pool, blk, te, ta, xa, ha)
+        runtime.stage_batch(pool, blk, te, tb, xb, hb)
+        torch.cuda.synchronize()
+        if concurrent:
+            s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+            for _ in range(3):
+                runtime.stage_batch(pool, blk, te, ta, xa, ha, cuda_stream=s1)
+                runtime.stage_batch(pool, blk, te, tb, xb, hb, cuda_stream=s2)
+        else:
+            for _ in range(3):
+                runtime.stage_batch(pool, blk, te, ta, xa, ha)
+                runtime.stage_batch(pool, blk, te, tb, xb, hb)
+        torch.cuda.synchronize()
+        kv = [pool.fetch(sg, 0, s, c % R) for (sg, s) in
+              [(i, 0) for i in range(n_per)] + [(n_per + i, cfg.n_steps - 1) for i in range(n_per)]]
+        return host(ha), host(hb), [host(k) for k, _ in kv] + [host(v) for _, v in kv]
+
+    seq, conc = run(False), run(True)
+    np.testing.assert_array_equal(conc[0], seq[0])
+    np.testing.assert_array_equal(conc[1], seq[1])
+    for a, b in zip(conc[2], seq[2]):
+        np.testing.assert_array_equal(a, b)
+
+
 def test_head_rejects_bad_arguments():
     cfg = C3
     hw = {k: to_dev(v.T if v.ndim == 2 and k.startswith("w") else v,
