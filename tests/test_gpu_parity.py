@@ -162,6 +162,19 @@ def test_stage_c2_single_task_full():
     _check_case(case)
 
 
+def test_stage_batch_invariance_bitwise_c2_shape():
+    """A task's stage output and cache entries do not depend on its batch: at
+    the 1.3B shape, batch 1 (M = 1560 rows) and batch 2 (M = 3120) take other
+    GEMM row tiles and grids, and the task's results are bitwise equal."""
+    a = StageCase(C2, [(0, 7, 2, 3)]).run_gpu()
+    b = StageCase(C2, [(0, 7, 2, 3), (1, 7, 1, 3)]).run_gpu()
+    L = C2.tokens
+    assert a.h_in.shape[0] == L and np.array_equal(a.h_in, b.h_in[:L])
+    assert np.array_equal(a.gpu_h_out, b.gpu_h_out[:L])
+    for x, y in zip(a.gpu_kv[(0, 7, 2)], b.gpu_kv[(0, 7, 2)]):
+        assert np.array_equal(x, y)
+
+
 def test_stage_c3_mixed_steps_sampled():
     """1.3B shape, a time-shared batch of 8 tasks: 2 chunks per step at all 4
     steps (k = 2, ring W + 2); sampled rows of two tasks checked."""
