@@ -9,8 +9,8 @@
 //
 // Tiling: 256 x 256 macro tile, 4 waves in a 2 x 2 grid, each owning a
 // 128 x 128 sub-tile = 4 x 4 MFMA 32x32 accumulators (in AGPRs); or, where it
-// fills the CUs' last round better, 192 x 256 tiles of 96 x 128 per wave
-// (3 x 4 accumulators).  Every output element sees the same MFMA sequence
+// fills the CUs' rounds better, 192 x 256 or 128 x 256 tiles of 96 x 128 or
+// 64 x 128 per wave (3 x 4 or 2 x 4 accumulators).  Every output element sees the same MFMA sequence
 // over K either way, so the choice never changes a result.  K advances
 // in stages of 128 bytes per row (64 bf16 / 32 fp32 = four MFMA k-units)
 // through two LDS stages filled by memory-to-LDS copies.  Operand chunks are
@@ -433,7 +433,9 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
         if (i < 2) {
           fr[fs][4 + 2 * i] = st[(BM + wn * 128 + (2 * i) * 32 + l32) * CPR + ch];
           fr[fs][5 + 2 * i] = st[(BM + wn * 128 + (2 * i + 1) * 32 + l32) * CPR + ch];
-        } else {
+          // two groups only (128-row tiles): each also reads its A fragment
+          if constexpr (MI == 2) fr[fs][i] = st[(wm * MR + i * 32 + l32) * CPR + ch];
+        } else if constexpr (MI > 2) {
           // A fragments [a0, a1) of the next unit in group i
           const int a0 = (i - 2) * MI / (MI - 2), a1 = (i - 1) * MI / (MI - 2);
 #pragma unroll
@@ -483,10 +485,11 @@ __global__ void __launch_bounds__(NT) k_gemm(const T* __restrict__ A, const T* _
   for (int st = 0; st < NSTAGE && st < nk; ++st)
 #pragma unroll
     for (int c = 0; c < IPWA + IPWB; ++c) dma_one(st, c);
-  static_assert(IPWA + IPWB == 14 || IPWA + IPWB == 16, "prologue wait counts 14 or 16 copies");
+  static_assert(IPWA + IPWB == 12 || IPWA + IPWB == 14 || IPWA + IPWB == 16, "prologue waits for 12, 14 or 16");
   if (nk > 1) {   // stage 0 landed, stage 1 may fly
     if constexpr (IPWA + IPWB == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    else if constexpr (IPWA + IPWB == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   }
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -588,12 +591,15 @@ hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, i
     return hipErrorInvalidValue;
   // Row tile: the one with the shorter estimated run, in rounds of tiles
   // over all CUs.  A round of 192-row tiles measured 0.82-0.91 of a round of
-  // 256-row ones (fewer rows per copied byte); it is counted as 0.85 (17/20).
-  // Ties keep 256 rows.
+  // 256-row ones (fewer rows per copied byte) and is counted as 0.85 (17/20);
+  // a round of 128-row tiles measured 0.69 and is counted as 0.7 (14/20).
+  // The 128-row tile only wins when few tiles leave CUs idle (small batches).
+  // Ties keep the larger tile.
   const int cu = cu_count(), tn = (N + BN - 1) / BN;
   auto rounds = [&](int bm) { return (int64_t)((((M + bm - 1) / bm) * tn + cu - 1) / cu); };
-  if (rounds(RowTile<3>::BM) * 17 < rounds(RowTile<4>::BM) * 20)
-    return launch_gemm_mi<T, 3>(epi, A, lda, B, M, N, K, ep, tt, s);
+  const int64_t c4 = rounds(RowTile<4>::BM) * 20, c3 = rounds(RowTile<3>::BM) * 17, c2 = rounds(RowTile<2>::BM) * 14;
+  if (c2 < c3 && c2 < c4) return launch_gemm_mi<T, 2>(epi, A, lda, B, M, N, K, ep, tt, s);
+  if (c3 < c4) return launch_gemm_mi<T, 3>(epi, A, lda, B, M, N, K, ep, tt, s);
   return launch_gemm_mi<T, 4>(epi, A, lda, B, M, N, K, ep, tt, s);
 }
 
