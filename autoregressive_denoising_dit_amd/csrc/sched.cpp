@@ -107,6 +107,7 @@ struct ps_sched {
   }
 
   // depth-first placement of ranks r.. with at most `left` discrepancies
+  // (recursion depth = rank count <= n_blocks * n_steps <= 4096)
   bool dfs(int r, int left, std::vector<int>& chosen) {
     if (r == (int)ranks.size()) return true;
     const std::vector<int> cand = candidates(ranks[r]);
@@ -130,7 +131,7 @@ extern "C" ps_status ps_sched_create(const ps_sched_desc* desc, ps_sched** out) 
   if (!desc || !out) return ps::set_error(PS_ERR_INVALID_ARG, "ps_sched_create: null argument");
   const ps_sched_desc& d = *desc;
   if (d.n_gpus < 1 || d.positions < 1 || d.n_blocks < 1 || d.n_steps < 1 || d.max_discrepancy < 0 ||
-      (int64_t)d.n_blocks * d.n_steps > (1 << 16) || !(d.slo_ms > 0) || !(d.batch_fixed_ms >= 0) ||
+      (int64_t)d.n_blocks * d.n_steps > (1 << 12) || !(d.slo_ms > 0) || !(d.batch_fixed_ms >= 0) ||
       !(d.batch_task_ms > 0) || d.ranks_per_stream < 0)
     return ps::set_error(PS_ERR_INVALID_ARG, "ps_sched_create: field out of range");
   ps_sched* s = new (std::nothrow) ps_sched;

@@ -46,7 +46,7 @@ typedef struct ps_sched_desc {
   int32_t n_gpus;            /* physical GPUs, >= 1 */
   int32_t positions;         /* virtual ranks one GPU can hold, >= 1 */
   int32_t n_blocks;          /* Transformer blocks of the model, >= 1 */
-  int32_t n_steps;           /* denoising steps, >= 1; n_blocks * n_steps <= 1 << 16 */
+  int32_t n_steps;           /* denoising steps, >= 1; n_blocks * n_steps <= 4096 */
   int32_t max_discrepancy;   /* LDS limit, >= 0 */
   int32_t ranks_per_stream;  /* 0: the fewest that meet the SLO alone; else exactly this many (<= stages) */
   double slo_ms;             /* chunk-interval target, > 0 */

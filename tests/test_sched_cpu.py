@@ -81,3 +81,12 @@ def test_errors():
         s.gpu(2)
     tiny = Scheduler(2, 2, 4, 2, 1.0, 1.0, 1.0)   # a single stage costs 2 > SLO
     assert tiny.split() == 0 and tiny.admit(1) is None
+
+
+@needs_lib
+def test_stage_count_limit():
+    from autoregressive_denoising_dit_amd.sched import Scheduler
+    from autoregressive_denoising_dit_amd._lib import PsError
+    Scheduler(2, 2, 64, 64, 10.0, 0.0, 1.0)          # 4096 stages: accepted
+    with pytest.raises(PsError):
+        Scheduler(2, 2, 64, 65, 10.0, 0.0, 1.0)      # 4160 stages: refused
