@@ -30,7 +30,7 @@ PS_FREQ_DIM = 256
 EXPORTS = (
     "ps_kv_pool_create", "ps_kv_pool_destroy", "ps_kv_pool_load", "ps_kv_pool_fetch",
     "ps_context_fetch", "ps_block_create", "ps_block_destroy", "ps_time_embed_create",
-    "ps_time_embed_destroy", "ps_time_embed_get", "ps_context_set", "ps_stage_batch",
+    "ps_time_embed_destroy", "ps_time_embed_get", "ps_context_set", "ps_stage_batch", "ps_stage_batch_probe",
     "ps_euler_update", "ps_last_error", "ps_trace_enable", "ps_trace_collect", "ps_trace_count",
     "ps_trace_entry", "ps_head_create", "ps_head_destroy", "ps_patch_embed", "ps_output_head",
     "ps_sched_create", "ps_sched_destroy", "ps_sched_split", "ps_sched_admit", "ps_sched_release",
@@ -72,6 +72,14 @@ class SchedDesc(C.Structure):
                 ("batch_fixed_ms", C.c_double), ("batch_task_ms", C.c_double)]
 
 
+PROBE_FIELDS = ("y1", "q", "attn", "h1", "y2", "q2", "xattn", "h2", "y3", "u")
+PROBE_FP32 = ("h1", "h2")   # the others are in the compute dtype
+
+
+class StageProbe(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in PROBE_FIELDS]
+
+
 class Task(C.Structure):
     _fields_ = [("stream", C.c_int32), ("chunk", C.c_int32), ("step", C.c_int32),
                 ("timestep", C.c_float), ("write_slot", C.c_int32), ("n_read", C.c_int32),
@@ -105,6 +113,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ps_time_embed_get": [vp, f32, vp, vp],
         "ps_context_set": [vp, vp, i32, vp, i32, vp],
         "ps_stage_batch": [vp, vp, vp, C.POINTER(Task), i32, vp, vp, vp],
+        "ps_stage_batch_probe": [vp, vp, vp, C.POINTER(Task), i32, vp, vp, C.POINTER(StageProbe), vp],
         "ps_euler_update": [vp, vp, C.POINTER(C.c_float), i32, i32, i32, i32, vp],
         "ps_head_create": [C.POINTER(HeadDesc), C.POINTER(vp)],
         "ps_head_destroy": [vp],

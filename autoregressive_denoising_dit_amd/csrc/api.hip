@@ -546,9 +546,26 @@ extern "C" ps_status ps_context_set(ps_kv_pool* p, const ps_block* b, int32_t st
 // same memory channel (a dense stride of 5120 or 13824 bf16 elements does).
 static int act_ld(int cols) { return cols + 64; }
 
+// Copy of a [rows, cols] activation stored with row stride ld into a dense
+// caller buffer (a probe member; nothing when it is null).
+static ps_status probe_copy(void* dst, const void* src, size_t es, size_t rows, int cols, int ld, hipStream_t hs) {
+  if (!dst) return PS_OK;
+  PS_HIP(hipMemcpy2DAsync(dst, cols * es, src, ld * es, cols * es, rows, hipMemcpyDeviceToDevice, hs));
+  return PS_OK;
+}
+
+#define PS_PROBE(member, src, cols, ld)                                                            \
+  do {                                                                                             \
+    if (pr) {                                                                                      \
+      ps_status ps_ = probe_copy(pr->member, src, sizeof(*(src)), (size_t)M, cols, ld, hs);         \
+      if (ps_) return ps_;                                                                         \
+    }                                                                                              \
+  } while (0)
+
 template <typename T>
 static ps_status run_stage(ps_kv_pool* p, ps_kv_pool::Workspace* w, const ps_block* b, const DevTask* tt, int n,
-                           const float* mod, const float2* rope_f, const float* h_in, float* h_out, hipStream_t hs) {
+                           const float* mod, const float2* rope_f, const float* h_in, float* h_out,
+                           const ps_stage_probe* pr, hipStream_t hs) {
   const ps_block_desc& bd = b->d;
   const int L = p->L(), D = bd.hidden, F = bd.ffn, M = n * L;
   T* y = static_cast<T*>(w->y.p);
@@ -562,6 +579,7 @@ static ps_status run_stage(ps_kv_pool* p, ps_kv_pool::Workspace* w, const ps_blo
   // self-attention branch
   const int ldy = act_ld(D), ldu = act_ld(F);
   PS_TRACED("ln1", (launch_layernorm<T>(h_in, y, ldy, M, D, mod, 0, 1, L, hs)));
+  PS_PROBE(y1, y, D, ldy);
   EpiArgs e1;
   e1.bias = bd.bqkv;
   e1.out = q;
@@ -572,7 +590,9 @@ static ps_status run_stage(ps_kv_pool* p, ps_kv_pool::Workspace* w, const ps_blo
   e1.d_shift = bd.head_dim == 128 ? 7 : 6;
   W = static_cast<const T*>(bd.wqkv);
   PS_TRACED("qkv", (launch_gemm<T>(EPI_QKV, y, ldy, W, M, 3 * D, D, e1, tt, hs)));
+  PS_PROBE(q, q, D, D);
   PS_TRACED("attn_self", (launch_attention<T>(false, q, a, ldy, pg, tt, n, hs)));
+  PS_PROBE(attn, a, D, ldy);
   EpiArgs e2;
   e2.bias = bd.bo;
   e2.h_in = h_in;
@@ -582,16 +602,20 @@ static ps_status run_stage(ps_kv_pool* p, ps_kv_pool::Workspace* w, const ps_blo
   e2.L = L;
   e2.div_L = FastDiv((uint32_t)L);
   PS_TRACED("o_proj", (launch_gemm<T>(EPI_RES, a, ldy, static_cast<const T*>(bd.wo), M, D, D, e2, tt, hs)));
+  PS_PROBE(h1, h_out, D, D);
 
   // cross-attention branch
   PS_TRACED("ln2", (launch_layernorm<T>(h_out, y, ldy, M, D, nullptr, -1, -1, L, hs)));
+  PS_PROBE(y2, y, D, ldy);
   EpiArgs e3;
   e3.bias = bd.bq2;
   e3.out = q;
   e3.ldo = D;
   e3.out_scale = qscale;
   PS_TRACED("xq_proj", (launch_gemm<T>(EPI_STORE, y, ldy, static_cast<const T*>(bd.wq2), M, D, D, e3, tt, hs)));
+  PS_PROBE(q2, q, D, D);
   PS_TRACED("attn_cross", (launch_attention<T>(true, q, a, ldy, pg, tt, n, hs)));
+  PS_PROBE(xattn, a, D, ldy);
   EpiArgs e4;
   e4.bias = bd.bo2;
   e4.h_in = h_out;
@@ -599,14 +623,17 @@ static ps_status run_stage(ps_kv_pool* p, ps_kv_pool::Workspace* w, const ps_blo
   e4.L = L;
   e4.div_L = FastDiv((uint32_t)L);
   PS_TRACED("xo_proj", (launch_gemm<T>(EPI_RES, a, ldy, static_cast<const T*>(bd.wo2), M, D, D, e4, tt, hs)));
+  PS_PROBE(h2, h_out, D, D);
 
   // FFN branch
   PS_TRACED("ln3", (launch_layernorm<T>(h_out, y, ldy, M, D, mod, 3, 4, L, hs)));
+  PS_PROBE(y3, y, D, ldy);
   EpiArgs e5;
   e5.bias = bd.b1;
   e5.out = u;
   e5.ldo = ldu;
   PS_TRACED("ffn1", (launch_gemm<T>(EPI_GELU, y, ldy, static_cast<const T*>(bd.w1), M, F, D, e5, tt, hs)));
+  PS_PROBE(u, u, F, ldu);
   EpiArgs e6;
   e6.bias = bd.b2;
   e6.h_in = h_out;
@@ -619,8 +646,8 @@ static ps_status run_stage(ps_kv_pool* p, ps_kv_pool::Workspace* w, const ps_blo
   return PS_OK;
 }
 
-extern "C" ps_status ps_stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const ps_task* tasks,
-                                    int32_t n, const float* h_in, float* h_out, hipStream_t hs) {
+static ps_status stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const ps_task* tasks, int32_t n,
+                             const float* h_in, float* h_out, const ps_stage_probe* probe, hipStream_t hs) {
   if (!p || !b || !te || !tasks || !h_in || !h_out) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: null argument");
   if (n < 1 || n > PS_MAX_TASKS) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: n_tasks %d not in [1, %d]", n, PS_MAX_TASKS);
   const ps_pool_desc& pd = p->desc;
@@ -712,12 +739,24 @@ extern "C" ps_status ps_stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_em
   PS_TRACED("modulation", launch_modulation(te->cache, rows.data(), bd.tmod, mod, rope_f, dtasks, n, D, pd.frames, p->seg_f, hs));
 
   if (bd.dtype == PS_BF16)
-    st = run_stage<bf16>(p, w, b, dtasks, n, mod, rope_f, h_in, h_out, hs);
+    st = run_stage<bf16>(p, w, b, dtasks, n, mod, rope_f, h_in, h_out, probe, hs);
   else
-    st = run_stage<float>(p, w, b, dtasks, n, mod, rope_f, h_in, h_out, hs);
+    st = run_stage<float>(p, w, b, dtasks, n, mod, rope_f, h_in, h_out, probe, hs);
   if (st) return st;
   for (int i = 0; i < n; ++i) p->ledger[writes[i]] = tasks[i].chunk;
   return PS_OK;
+}
+
+extern "C" ps_status ps_stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const ps_task* tasks,
+                                    int32_t n, const float* h_in, float* h_out, hipStream_t hs) {
+  return stage_batch(p, b, te, tasks, n, h_in, h_out, nullptr, hs);
+}
+
+extern "C" ps_status ps_stage_batch_probe(ps_kv_pool* p, const ps_block* b, ps_time_embed* te,
+                                          const ps_task* tasks, int32_t n, const float* h_in, float* h_out,
+                                          const ps_stage_probe* probe, hipStream_t hs) {
+  if (!probe) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch_probe: null probe");
+  return stage_batch(p, b, te, tasks, n, h_in, h_out, probe, hs);
 }
 
 // ------------------------------------------------------------------- head

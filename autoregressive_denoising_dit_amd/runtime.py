@@ -276,6 +276,27 @@ def stage_batch(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], h_in
                                   _stream_ptr(cuda_stream)))
 
 
+def stage_batch_probe(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], h_in: torch.Tensor,
+                      h_out: torch.Tensor, probe: Dict[str, torch.Tensor], cuda_stream=None) -> None:
+    """stage_batch that also copies the intermediates named in `probe`
+    (keys from _lib.PROBE_FIELDS, each a dense device tensor: [n*L, F] for
+    "u", [n*L, D] otherwise; fp32 for h1 / h2, the compute dtype otherwise)."""
+    n = len(tasks)
+    _need(h_in, torch.float32, (n * pool.tokens, pool.hidden), "h_in")
+    _need(h_out, torch.float32, (n * pool.tokens, pool.hidden), "h_out")
+    pr = _lib.StageProbe()
+    for name, t in probe.items():
+        if name not in _lib.PROBE_FIELDS:
+            raise ValueError(f"unknown probe member {name!r}")
+        dt = torch.float32 if name in _lib.PROBE_FP32 else TORCH_DTYPE[block.dtype]
+        cols = block.ffn if name == "u" else pool.hidden
+        _need(t, dt, (n * pool.tokens, cols), name)
+        setattr(pr, name, t.data_ptr())
+    arr = (Task * max(n, 1))(*tasks)
+    check(pool.lib.ps_stage_batch_probe(pool.handle, block.handle, te.handle, arr, n, _ptr(h_in), _ptr(h_out),
+                                        C.byref(pr), _stream_ptr(cuda_stream)))
+
+
 def euler_update(x: torch.Tensor, v: torch.Tensor, dt: Sequence[float], tokens: int, hidden: int,
                  cuda_stream=None) -> None:
     n = len(dt)

@@ -200,6 +200,44 @@ ps_status ps_stage_batch(ps_kv_pool* pool, const ps_block* block, ps_time_embed*
                          const ps_task* tasks, int32_t n_tasks, const float* h_in,
                          float* h_out, hipStream_t hs);
 
+/* Intermediate activations of one stage batch, for checking each kernel of
+ * the path on its own.  Every member is a caller-owned device pointer or
+ * NULL (not captured); row i*L + r belongs to task i, rows dense.  Members in
+ * the compute dtype ("dt") are the values the next kernel consumes, as stored:
+ *   y1    dt [n*L, D]  LN(h)(1 + scale1) + shift1
+ *   q     dt [n*L, D]  self-attention queries after RoPE3D, multiplied by
+ *                      log2(e)/sqrt(head_dim) (the softmax works in base 2)
+ *   attn  dt [n*L, D]  self-attention output, before wo
+ *   h1    fp32 [n*L, D] residual stream after the self-attention branch
+ *   y2    dt [n*L, D]  LN(h1)
+ *   q2    dt [n*L, D]  cross-attention queries, same scaling as q
+ *   xattn dt [n*L, D]  cross-attention output, before wo2
+ *   h2    fp32 [n*L, D] residual stream after the cross-attention branch
+ *   y3    dt [n*L, D]  LN(h2)(1 + scale2) + shift2
+ *   u     dt [n*L, F]  GELU_tanh(y3 w1^T + b1)
+ * (AREX article on the PhysisServe report, section "三层设计": a stage is one
+ * block at one step; the block's steps are those of ps_stage_batch.) */
+typedef struct {
+  void* y1;
+  void* q;
+  void* attn;
+  float* h1;
+  void* y2;
+  void* q2;
+  void* xattn;
+  float* h2;
+  void* y3;
+  void* u;
+} ps_stage_probe;
+
+/* ps_stage_batch that also copies the intermediates `probe` asks for (device
+ * to device, on hs, after the kernel that produces each).  Same arguments,
+ * results and errors as ps_stage_batch, plus PS_ERR_INVALID_ARG for a NULL
+ * probe.  The copies make it slower: it is for tests and debugging. */
+ps_status ps_stage_batch_probe(ps_kv_pool* pool, const ps_block* block, ps_time_embed* te,
+                               const ps_task* tasks, int32_t n_tasks, const float* h_in,
+                               float* h_out, const ps_stage_probe* probe, hipStream_t hs);
+
 /* ------------------------------------------------------------------ head --
  * The steps either side of the block stack (a Wan-style reading; the pages
  * evaluate Wan-family backbones -- AREX article on the PhysisServe report,

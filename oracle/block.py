@@ -151,12 +151,13 @@ def context_kv(ctx, w, heads):
     return kv[:, :D].reshape(-1, heads, D // heads), kv[:, D:].reshape(-1, heads, D // heads)
 
 
-def qkv_phase(h, mod, w, chunk, grid, heads):
+def qkv_phase(h, mod, w, chunk, grid, heads, trace=None):
     """Self-attention inputs of one task: y = LN(h)(1 + scale1) + shift1;
     q, k, v = y Wqkv + b; RoPE3D on q and k at the chunk's token positions.
 
     Returns q, k, v, each [L, H, d]; (k, v) is what the chunk leaves in the
-    noisy-KV cache at this (block, step)."""
+    noisy-KV cache at this (block, step).  A dict passed as ``trace`` receives
+    the intermediates y1 and q ([L, D])."""
     h = np.asarray(h, dtype=F64)
     L, D = h.shape
     d = D // heads
@@ -166,10 +167,13 @@ def qkv_phase(h, mod, w, chunk, grid, heads):
     k = qkv[:, D:2 * D].reshape(L, heads, d)
     v = qkv[:, 2 * D:].reshape(L, heads, d)
     pos = token_positions(chunk, grid)
-    return rope3d(q, pos), rope3d(k, pos), v
+    q, k = rope3d(q, pos), rope3d(k, pos)
+    if trace is not None:
+        trace["y1"], trace["q"] = y, q.reshape(L, D)
+    return q, k, v
 
 
-def rest_phase(h, q, K, V, mod, w, ctx_k, ctx_v, rows=None):
+def rest_phase(h, q, K, V, mod, w, ctx_k, ctx_v, rows=None, trace=None):
     """The rest of the block once the window's keys/values are known.
 
     K, V: [keys, H, d], the window's chunks oldest first then the chunk itself.
@@ -177,7 +181,9 @@ def rest_phase(h, q, K, V, mod, w, ctx_k, ctx_v, rows=None):
       h <- h + CrossAttn(LN(h) Wq2 + bq2, ctx_k, ctx_v) Wo2 + bo2
       h <- h + gate2 * (GELU_tanh((LN(h)(1 + scale2) + shift2) W1 + b1) W2 + b2)
     ``rows`` (optional) restricts the computation to those query rows; every
-    step after the attention is row-wise, so the result rows are unchanged."""
+    step after the attention is row-wise, so the result rows are unchanged.
+    A dict passed as ``trace`` receives the intermediates attn, h1, y2, q2,
+    xattn, h2, y3 and u (the FFN hidden activation), for those rows."""
     h = np.asarray(h, dtype=F64)
     if rows is not None:
         h = h[rows]
@@ -185,24 +191,28 @@ def rest_phase(h, q, K, V, mod, w, ctx_k, ctx_v, rows=None):
     L, D = h.shape
     heads = q.shape[1]
     a = attention(q, K, V).reshape(L, D)
-    h = h + mod[2] * _lin(a, w["wo"], w["bo"])
-    y2 = layer_norm(h)
+    h1 = h + mod[2] * _lin(a, w["wo"], w["bo"])
+    y2 = layer_norm(h1)
     q2 = _lin(y2, w["wq2"], w["bq2"]).reshape(L, heads, D // heads)
     a2 = attention(q2, ctx_k, ctx_v).reshape(L, D)
-    h = h + _lin(a2, w["wo2"], w["bo2"])
-    y3 = layer_norm(h) * (1.0 + mod[4]) + mod[3]
-    h = h + mod[5] * _lin(gelu_tanh(_lin(y3, w["w1"], w["b1"])), w["w2"], w["b2"])
-    return h
+    h2 = h1 + _lin(a2, w["wo2"], w["bo2"])
+    y3 = layer_norm(h2) * (1.0 + mod[4]) + mod[3]
+    u = gelu_tanh(_lin(y3, w["w1"], w["b1"]))
+    if trace is not None:
+        trace.update(attn=a, h1=h1, y2=y2, q2=q2.reshape(L, D), xattn=a2, h2=h2, y3=y3, u=u)
+    return h2 + mod[5] * _lin(u, w["w2"], w["b2"])
 
 
-def block_task(h, e, w, chunk, prior_kv, ctx_kv, grid, heads, rows=None):
+def block_task(h, e, w, chunk, prior_kv, ctx_kv, grid, heads, rows=None, trace=None):
     """One stage task: block ``w`` at the timestep whose embedding is ``e``.
 
     prior_kv: list of (K, V) of the window's earlier chunks, oldest first.
-    Returns (h_out, (k, v)) where (k, v) is this chunk's cache entry."""
+    Returns (h_out, (k, v)) where (k, v) is this chunk's cache entry.  A dict
+    passed as ``trace`` receives the block's intermediates (qkv_phase and
+    rest_phase; y1 and q over all rows, the rest over ``rows``)."""
     mod = modulation(e, w["tmod"])
-    q, k, v = qkv_phase(h, mod, w, chunk, grid, heads)
+    q, k, v = qkv_phase(h, mod, w, chunk, grid, heads, trace=trace)
     K = np.concatenate([kv[0] for kv in prior_kv] + [k], axis=0)
     V = np.concatenate([kv[1] for kv in prior_kv] + [v], axis=0)
-    h_out = rest_phase(h, q, K, V, mod, w, ctx_kv[0], ctx_kv[1], rows=rows)
+    h_out = rest_phase(h, q, K, V, mod, w, ctx_kv[0], ctx_kv[1], rows=rows, trace=trace)
     return h_out, (k, v)

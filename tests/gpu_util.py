@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 import oracle
-from autoregressive_denoising_dit_amd import runtime
+from autoregressive_denoising_dit_amd import _lib, runtime
 from synthetic import inputs
 
 BF16_TOL = 3e-2    # max |err| / RMS(ref), bf16 operands
@@ -87,7 +87,7 @@ class StageCase:
         self.h_in = inputs.hidden_rows(cfg, len(tasks), seed)
 
     # ---------------------------------------------------------------- GPU
-    def run_gpu(self, h_out_same=False):
+    def run_gpu(self, h_out_same=False, probe=False):
         cfg = self.cfg
         say("stage", cfg.name, "tasks", self.tasks)
         self.pool = make_pool(cfg, n_streams=self.n_streams, n_blocks=self.block_index + 1, n_slots=self.R)
@@ -102,7 +102,15 @@ class StageCase:
                     for (sg, c, s, nr) in self.tasks]
         h_in = to_dev(self.h_in, torch.float32)
         h_out = h_in if h_out_same else torch.empty_like(h_in)
-        runtime.stage_batch(self.pool, self.block, self.te, ps_tasks, h_in, h_out)
+        if probe:
+            M = len(self.tasks) * cfg.tokens
+            self.gpu_probe = {
+                name: torch.full((M, cfg.ffn if name == "u" else cfg.hidden), float("nan"), device="cuda",
+                                 dtype=torch.float32 if name in _lib.PROBE_FP32 else self.td)
+                for name in _lib.PROBE_FIELDS}
+            runtime.stage_batch_probe(self.pool, self.block, self.te, ps_tasks, h_in, h_out, self.gpu_probe)
+        else:
+            runtime.stage_batch(self.pool, self.block, self.te, ps_tasks, h_in, h_out)
         torch.cuda.synchronize()
         self.gpu_h_out = host(h_out)
         self.gpu_kv = {}
@@ -113,15 +121,21 @@ class StageCase:
         return self
 
     # ------------------------------------------------------------- oracle
-    def run_oracle(self, task_ids=None, rows=None):
-        """Oracle h_out rows (all or a sample) and cache entries of the tasks."""
+    def run_oracle(self, task_ids=None, rows=None, attn_rounding=False):
+        """Oracle h_out rows (all or a sample), cache entries of the tasks and
+        each task's intermediates (self.ref_trace[i]: y1 and q over all rows,
+        the rest over ``rows``).  With ``attn_rounding`` (bf16 workloads) the
+        trace also holds "attn_rb" and "xattn_rb": both attentions evaluated by
+        the oracle on its own queries, keys and values rounded to bf16, the
+        precision they are stored in -- a measure of how far that storage
+        alone moves the attention outputs."""
         cfg, L = self.cfg, self.cfg.tokens
         ids = range(len(self.tasks)) if task_ids is None else task_ids
         E = {s: oracle.time_embedding(t, self.tw) for s, t in enumerate(cfg.timesteps)}
         ctx_kv = {}
         # the batch's own writes land before any read (a task may read what
         # another task of the batch writes); computed for the tasks needed
-        own = {}
+        own, own_trace = {}, {}
         where = {(sg, s, c): i for i, (sg, c, s, _) in enumerate(self.tasks)}
 
         def qkv(key):
@@ -129,11 +143,12 @@ class StageCase:
                 i = where[key]
                 sg, c, s, _ = self.tasks[i]
                 mod = oracle.modulation(E[s], self.w["tmod"])
+                own_trace[key] = {}
                 own[key] = oracle.qkv_phase(self.h_in[i * L:(i + 1) * L], mod, self.w, c, cfg.grid,
-                                            cfg.heads)
+                                            cfg.heads, trace=own_trace[key])
             return own[key]
 
-        out = {}
+        out, self.ref_trace = {}, {}
         for i in ids:
             sg, c, s, nr = self.tasks[i]
             mod = oracle.modulation(E[s], self.w["tmod"])
@@ -146,7 +161,21 @@ class StageCase:
             h = self.h_in[i * L:(i + 1) * L]
             if sg not in ctx_kv:
                 ctx_kv[sg] = oracle.context_kv(self.ctx[sg], self.w, cfg.heads)
-            out[i] = oracle.rest_phase(h, q, K, V, mod, self.w, *ctx_kv[sg], rows=rows)
+            tr = dict(own_trace[(sg, s, c)])
+            out[i] = oracle.rest_phase(h, q, K, V, mod, self.w, *ctx_kv[sg], rows=rows, trace=tr)
+            if attn_rounding and cfg.dtype == "bf16":
+                def rb(a):
+                    return inputs.round_bf16(np.asarray(a, np.float32)).astype(np.float64)
+                qr = q if rows is None else q[rows]
+                n_r = qr.shape[0]
+                tr["attn_rb"] = oracle.attention(rb(qr), rb(K), rb(V)).reshape(n_r, cfg.hidden)
+                tr["xattn_rb"] = oracle.attention(rb(tr["q2"]).reshape(qr.shape), rb(ctx_kv[sg][0]),
+                                                  rb(ctx_kv[sg][1])).reshape(n_r, cfg.hidden)
+                # the two attention branches' deltas of the residual stream with those outputs
+                f64 = lambda a: np.asarray(a, np.float64)
+                tr["h1 - h_rb"] = mod[2] * (tr["attn_rb"] @ f64(self.w["wo"]) + f64(self.w["bo"]))
+                tr["h2 - h1_rb"] = tr["xattn_rb"] @ f64(self.w["wo2"]) + f64(self.w["bo2"])
+            self.ref_trace[i] = tr
         self.ref_h_out = out
         self.ref_kv = {(sg, c, s): own[(sg, s, c)][1:] for (sg, c, s, _) in self.tasks if (sg, s, c) in own}
         return self

@@ -47,6 +47,7 @@ int main(void) {
          offsetof(ps_time_desc, wt1), offsetof(ps_task, read_slots));
   printf("%zu %zu %zu %zu\n", sizeof(ps_head_desc), offsetof(ps_head_desc, w_embed), sizeof(ps_sched_desc),
          offsetof(ps_sched_desc, slo_ms));
+  printf("%zu %zu %zu\n", sizeof(ps_stage_probe), offsetof(ps_stage_probe, h1), offsetof(ps_stage_probe, u));
   return 0;
 }
 ''')
@@ -60,7 +61,8 @@ int main(void) {
     want = [C.sizeof(_lib.PoolDesc), C.sizeof(_lib.BlockDesc), C.sizeof(_lib.TimeDesc), C.sizeof(_lib.Task),
             _lib.BlockDesc.wqkv.offset, _lib.BlockDesc.tmod.offset, _lib.TimeDesc.wt1.offset,
             _lib.Task.read_slots.offset, C.sizeof(_lib.HeadDesc), _lib.HeadDesc.w_embed.offset,
-            C.sizeof(_lib.SchedDesc), _lib.SchedDesc.slo_ms.offset]
+            C.sizeof(_lib.SchedDesc), _lib.SchedDesc.slo_ms.offset,
+            C.sizeof(_lib.StageProbe), _lib.StageProbe.h1.offset, _lib.StageProbe.u.offset]
     assert got == want
 
 
@@ -88,6 +90,10 @@ def test_validation_fails_before_device_work():
     td = _lib.TimeDesc(128, 0, *([16] * 6))                     # zero capacity
     assert lib.ps_time_embed_create(C.byref(td), C.byref(h)) == _lib.PS_ERR_INVALID_ARG
     assert lib.ps_stage_batch(None, None, None, None, 1, None, None, None) == _lib.PS_ERR_INVALID_ARG
+    assert lib.ps_stage_batch_probe(None, None, None, None, 1, None, None, None, None) == _lib.PS_ERR_INVALID_ARG
+    assert b"probe" in lib.ps_last_error()
+    pr = _lib.StageProbe()
+    assert lib.ps_stage_batch_probe(None, None, None, None, 1, None, None, C.byref(pr), None) == _lib.PS_ERR_INVALID_ARG
     dt = (C.c_float * 1)(0.5)
     assert lib.ps_euler_update(None, None, dt, 1, 64, 128, 0, None) == _lib.PS_ERR_INVALID_ARG
     assert lib.ps_euler_update(C.c_void_p(16), C.c_void_p(16), dt, 0, 64, 128, 0, None) == _lib.PS_ERR_INVALID_ARG

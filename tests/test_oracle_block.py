@@ -198,8 +198,9 @@ def test_rope_invariants():
 
 
 # ---------------------------------------------------------------- the whole block
-def _torch_block(h, e, w, chunk, prior, ctx, grid, H):
-    """An independent statement of the block with torch library routines."""
+def _torch_block(h, e, w, chunk, prior, ctx, grid, H, trace=None):
+    """An independent statement of the block with torch library routines
+    (``trace``: a dict that receives the intermediates)."""
     L, D = h.shape
     d = D // H
     mod = T(e) + T(w["tmod"])
@@ -215,14 +216,20 @@ def _torch_block(h, e, w, chunk, prior, ctx, grid, H):
     V = torch.cat([T(p[1]) for p in prior] + [v])
     a = F.scaled_dot_product_attention(q.transpose(0, 1), K.transpose(0, 1), V.transpose(0, 1))
     x = x + gate1 * F.linear(a.transpose(0, 1).reshape(L, D), T(w["wo"]).T, T(w["bo"]))
+    tr = {"y1": y, "q": q.reshape(L, D), "attn": a.transpose(0, 1).reshape(L, D), "h1": x,
+          "y2": F.layer_norm(x, (D,), eps=1e-6)}
     q2 = F.linear(F.layer_norm(x, (D,), eps=1e-6), T(w["wq2"]).T, T(w["bq2"])).reshape(L, H, d)
     kv2 = F.linear(T(ctx), T(w["wkv2"]).T, T(w["bkv2"]))
     k2, v2 = [t.reshape(-1, H, d) for t in kv2.split(D, dim=1)]
     a2 = F.scaled_dot_product_attention(q2.transpose(0, 1), k2.transpose(0, 1), v2.transpose(0, 1))
     x = x + F.linear(a2.transpose(0, 1).reshape(L, D), T(w["wo2"]).T, T(w["bo2"]))
+    tr.update(q2=q2.reshape(L, D), xattn=a2.transpose(0, 1).reshape(L, D), h2=x)
     y3 = F.layer_norm(x, (D,), eps=1e-6) * (1 + scale2) + shift2
     f = F.gelu(F.linear(y3, T(w["w1"]).T, T(w["b1"])), approximate="tanh")
+    tr.update(y3=y3, u=f)
     x = x + gate2 * F.linear(f, T(w["w2"]).T, T(w["b2"]))
+    if trace is not None:
+        trace.update({n: t.numpy() for n, t in tr.items()})
     return x.numpy(), k.numpy(), v.numpy()
 
 
@@ -252,6 +259,36 @@ def test_block_matches_library_composition():
     np.testing.assert_allclose(v, rv, rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
     assert np.abs(got - h).max() > 0.1  # the branches did something
+
+
+def test_block_trace_matches_library_composition():
+    """Every intermediate the oracle records (each kernel's counterpart) against
+    the torch statement of the block, and the traced call's output against the
+    untraced one."""
+    cfg = _small_cfg()
+    r = np.random.default_rng(11)
+    w = _scaled_weights(cfg, 6)
+    L, D, H, d = cfg.tokens, cfg.hidden, cfg.heads, cfg.head_dim
+    h = r.standard_normal((L, D))
+    e = r.standard_normal((6, D))
+    prior = [(r.standard_normal((L, H, d)), r.standard_normal((L, H, d))) for _ in range(2)]
+    ctx = r.standard_normal((cfg.n_ctx, D))
+    ck = oracle.context_kv(ctx, w, H)
+    tr, ref_tr = {}, {}
+    got, _ = oracle.block_task(h, e, w, 5, prior, ck, cfg.grid, H, trace=tr)
+    plain, _ = oracle.block_task(h, e, w, 5, prior, ck, cfg.grid, H)
+    np.testing.assert_array_equal(got, plain)
+    _torch_block(h, e, w, 5, prior, ctx, cfg.grid, H, trace=ref_tr)
+    assert sorted(tr) == sorted(ref_tr) == sorted(["y1", "q", "attn", "h1", "y2", "q2", "xattn", "h2", "y3", "u"])
+    for name in tr:
+        assert tr[name].shape == (L, cfg.ffn if name == "u" else D), name
+        np.testing.assert_allclose(tr[name], ref_tr[name], rtol=1e-10, atol=1e-10, err_msg=name)
+    rows = np.array([1, 7])
+    part = {}
+    oracle.block_task(h, e, w, 5, prior, ck, cfg.grid, H, rows=rows, trace=part)
+    for name in part:
+        want = tr[name] if name in ("y1", "q") else tr[name][rows]
+        np.testing.assert_allclose(part[name], want, rtol=1e-13, atol=1e-13, err_msg=name)
 
 
 def test_block_rows_subset_equals_full():
