@@ -249,6 +249,27 @@ def test_stage_probe_kernels_c2_full():
     _check_probe(case)
 
 
+def test_stage_probe_kernels_c3_c4_sampled():
+    """Each kernel's output in a time-shared batch of 8 at the 1.3B shape (two
+    chunks per step at all four steps, one reading the other's same-batch
+    write) and in a 5B-shaped batch (1760-token chunks: ragged last query
+    and key tiles); sampled rows."""
+    tasks = []
+    for s in range(4):
+        for j in range(2):
+            c = 2 * (5 - s) + j
+            tasks.append((0, c, s, min(C3.window, c)))
+    case = StageCase(C3, tasks, n_slots=C3.window + 2).run_gpu(probe=True)
+    rows = np.array([0, 1, 100, 777, 1200, 1559])
+    case.run_oracle(task_ids=[1, 6], rows=rows, attn_rounding=True)
+    _check_probe(case, task_ids=[1, 6], rows=rows)
+    del case
+    case = StageCase(C4, [(0, 9, 3, 3), (0, 12, 0, 3)]).run_gpu(probe=True)
+    rows = np.array([0, 43, 44, 901, 1727, 1759])
+    case.run_oracle(task_ids=[0, 1], rows=rows, attn_rounding=True)
+    _check_probe(case, task_ids=[0, 1], rows=rows)
+
+
 def test_stage_probe_kernels_c5_sampled():
     """Each kernel's output in the 16-task batch of the 14B shape that the
     benchmark times (sampled rows of two tasks)."""
