@@ -400,7 +400,8 @@ def measured_traffic(kernel):
 
 
 def cpu_baseline(cfg, n_read, budget_s=30.0):
-    """The float64 CPU oracle on one task of the workload (a bounded sample)."""
+    """The float64 CPU oracle on whole stage tasks of the workload (a bounded
+    sample of about ten seconds): oracle stage tasks per second."""
     import numpy as np
     import oracle
     from synthetic import inputs, stage_flops
@@ -430,6 +431,17 @@ def cpu_baseline(cfg, n_read, budget_s=30.0):
             "sample": f"{done} whole {cfg.name} stage task(s) (all {L} query rows, {n_read} prior chunks "
                       f"+ own chunk of keys, {cfg.n_ctx} context tokens) in float64 NumPy: "
                       f"{dt:.1f} s measured"}
+
+
+def cpu_baseline_interval(cfg):
+    """The oracle's chunk interval of the staggered schedule, extrapolated from
+    timed whole stage tasks: a chunk takes one task per (block, step), and the
+    oracle runs them one after another."""
+    r = cpu_baseline(cfg, cfg.window)
+    per_chunk = cfg.n_blocks * cfg.n_steps
+    return {"value": round(per_chunk / r["value"] * 1e3, 1), "unit": "ms per chunk", "cores": r["cores"],
+            "kind": "oracle",
+            "sample": r["sample"] + f"; extrapolated to the {per_chunk} tasks (blocks x steps) of one chunk"}
 
 
 def main():
@@ -492,6 +504,7 @@ def main():
             "stage_tasks_per_s": round(cfg.n_blocks * cfg.n_steps * cfg.k / (tick * 1e-3), 1),
             "mfma_frac": round(per_chunk / (interval * 1e-3) / PEAK[cfg.dtype], 4),
             "kernel_ms_per_tick": per_tick,
+            **({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_interval(cfg)}),
         }), flush=True)
         return
     cfg = get(args.workload)
