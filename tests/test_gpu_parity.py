@@ -317,6 +317,21 @@ def test_stage_c3_mixed_steps_sampled():
     _check_case(case, task_ids=[1, 6], rows=rows)
 
 
+def test_stage_bf16_largest_batch_c3_shape():
+    """The most tasks one batch takes (32) at the 1.3B shape: 4 streams x 4
+    steps x 2 chunks, the second chunk of each pair reading the first one's
+    same-batch write (M = 49920 rows: 256-row eight-wave GEMM tiles, 12480
+    attention workgroups); sampled rows of three tasks, one per stream end."""
+    cfg = C3
+    tasks = [(sg, 2 * (5 - s) + j, s, C3.window) for sg in range(4) for s in range(4) for j in range(2)]
+    assert len(tasks) == 32
+    case = StageCase(cfg, tasks, n_slots=cfg.window + 2).run_gpu()
+    rows = np.array([0, 255, 256, 1535, 1559])
+    ids = [0, 13, 31]
+    case.run_oracle(task_ids=ids, rows=rows)
+    _check_case(case, task_ids=ids, rows=rows)
+
+
 def test_stage_c4_sampled():
     cfg = C4
     tasks = [(0, 9, 3, 3), (0, 12, 0, 3)]
