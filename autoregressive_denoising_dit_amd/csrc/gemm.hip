@@ -59,7 +59,7 @@ struct Tile {
   static constexpr int IPWB = (BN / NW) / RPI;        // B copy instructions per wave per stage
   static constexpr int STAGE_CH = (BM + BN) * CPR;    // 16-byte chunks per stage
   static_assert(IPWA * RPI * NW == BM && IPWB * RPI * NW == BN, "tile must split evenly over the copies");
-  static_assert(NW == 4 || (NW == 8 && MI == 4), "eight waves only with 256-row tiles");
+  static_assert(NW == 4 || (NW == 8 && MI >= 3), "eight waves only with 192- and 256-row tiles");
 };
 constexpr int STAGE_BYTES = 4 * 128 * EP * 4;          // 4 waves x 128 rows (or 8 x 64) x pitch
 constexpr int SMEM_BYTES = OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES;
@@ -307,13 +307,13 @@ __device__ __forceinline__ void epilogue_res(float* stg, StageFn stage_half, int
   }
 }
 
-// The same over a wave's 128 x 64 block (eight-wave tiles), staged in two
-// halves of 64 rows.
-template <typename StageFn>
+// The same over a wave's MR x 64 block (eight-wave tiles, MR = 96 or 128),
+// staged in two halves of 64 rows (the second one partly filled when MR = 96).
+template <int MR, typename StageFn>
 __device__ __forceinline__ void epilogue_res_rows(float* stg, StageFn stage_half, int rbase, int cbase, int lane,
                                                   int M, int N, const EpiArgs& ep, const char* tab, int n0) {
   constexpr int EB = 8, RB = 4 * EB, NB = 64 / RB;   // rows per batch, batches per half
-  const int nrows = min(128, M - rbase);
+  const int nrows = min(MR, M - rbase);
   if (nrows <= 0 || cbase >= N) return;
   const int rq = lane >> 4, cq = lane & 15;
   const int col = cbase + 4 * cq;
@@ -552,13 +552,15 @@ __global__ void __launch_bounds__(64 * NW) k_gemm(const T* __restrict__ A, const
   for (int st = 0; st < NSTAGE && st < nk; ++st)
 #pragma unroll
     for (int c = 0; c < IPWA + IPWB; ++c) dma_one(st, c);
-  static_assert(IPWA + IPWB == 8 || IPWA + IPWB == 12 || IPWA + IPWB == 14 || IPWA + IPWB == 16,
-                "prologue waits for 8, 12, 14 or 16");
+  static_assert(IPWA + IPWB == 7 || IPWA + IPWB == 8 || IPWA + IPWB == 12 || IPWA + IPWB == 14 ||
+                    IPWA + IPWB == 16,
+                "prologue waits for 7, 8, 12, 14 or 16");
   if (nk > 1) {   // stage 0 landed, stage 1 may fly
     if constexpr (IPWA + IPWB == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else if constexpr (IPWA + IPWB == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
     else if constexpr (IPWA + IPWB == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (IPWA + IPWB == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
   }
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -602,27 +604,29 @@ __global__ void __launch_bounds__(64 * NW) k_gemm(const T* __restrict__ A, const
       }
     }
   } else {
-    // half h: rows 64 h .. 64 h + 63 of the wave's 128 x 64 block
+    // half h: rows 64 h .. 64 h + 63 of the wave's MR x 64 block (the second
+    // half holds 32 rows when MR = 96)
     float* stg = reinterpret_cast<float*>(smem) + wave * (64 * EP);
     auto stage_half = [&](int hlf) __attribute__((always_inline)) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+        for (int ii = 0; ii < 2; ++ii) {
+          if (2 * hlf + ii >= MI) continue;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = ii * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
             stg[row * EP + jj * 32 + l32] = acc[2 * hlf + ii][jj][r];
           }
+        }
     };
     if constexpr (EPI == EPI_RES) {
-      epilogue_res_rows(stg, stage_half, m0 + wm * MR, n0 + wn * WC, lane, M, N, ep, tab, n0);
+      epilogue_res_rows<MR>(stg, stage_half, m0 + wm * MR, n0 + wn * WC, lane, M, N, ep, tab, n0);
     } else {
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        stage_half(hlf);
-        epilogue_block<T, EPI, 64>(stg, m0 + wm * MR + hlf * 64, n0 + wn * WC, lane, M, N, ep, tab, n0);
-      }
+      stage_half(0);
+      epilogue_block<T, EPI, 64>(stg, m0 + wm * MR, n0 + wn * WC, lane, M, N, ep, tab, n0);
+      stage_half(1);
+      epilogue_block<T, EPI, MR - 64>(stg, m0 + wm * MR + 64, n0 + wn * WC, lane, M, N, ep, tab, n0);
     }
   }
 }
@@ -694,12 +698,17 @@ hipError_t launch_gemm(int epi, const T* A, int lda, const T* B, int M, int N, i
   auto rounds = [&](int bm) { return (int64_t)((((M + bm - 1) / bm) * tn + cu - 1) / cu); };
   const int64_t c4 = rounds(Tile<4, 4>::BM) * 20, c3 = rounds(Tile<3, 4>::BM) * 17, c2 = rounds(Tile<2, 4>::BM) * 14;
   if (c2 < c3 && c2 < c4) return launch_gemm_mi<T, 2, 4>(epi, A, lda, B, M, N, K, ep, tt, s);
-  if (c3 < c4) return launch_gemm_mi<T, 3, 4>(epi, A, lda, B, M, N, K, ep, tt, s);
-  // 256-row tiles in bf16: eight waves up to K = 8192 (measured 2-13% faster
-  // on the 1.3B, 5B and 14B shapes there), four beyond (the long-K FFN2
-  // shapes ran 1-2% slower with eight)
+  // 192- and 256-row tiles in bf16: eight waves up to K = 8192 (measured 2-13%
+  // faster on the 1.3B, 5B and 14B shapes there), four beyond (the long-K
+  // FFN2 shapes ran 1-2% slower with eight)
+  const bool eight = std::is_same<T, bf16>::value && K <= 8192;
+  if (c3 < c4) {
+    if constexpr (std::is_same<T, bf16>::value)
+      if (eight) return launch_gemm_mi<T, 3, 8>(epi, A, lda, B, M, N, K, ep, tt, s);
+    return launch_gemm_mi<T, 3, 4>(epi, A, lda, B, M, N, K, ep, tt, s);
+  }
   if constexpr (std::is_same<T, bf16>::value)
-    if (K <= 8192) return launch_gemm_mi<T, 4, 8>(epi, A, lda, B, M, N, K, ep, tt, s);
+    if (eight) return launch_gemm_mi<T, 4, 8>(epi, A, lda, B, M, N, K, ep, tt, s);
   return launch_gemm_mi<T, 4, 4>(epi, A, lda, B, M, N, K, ep, tt, s);
 }
 
