@@ -608,6 +608,29 @@ def test_slot_ledger_rejects_stale_read():
     assert torch.isfinite(h).all()
 
 
+def test_pool_rejects_a_fifth_stream():
+    """A pool keeps one workspace per HIP stream for up to four streams; a
+    call on a fifth stream is refused before any launch, and the pool still
+    works on the streams it knows."""
+    cfg = C1
+    pool = make_pool(cfg, n_streams=1, n_blocks=1, check_slots=False)
+    blk = make_block(cfg, inputs.block_weights(cfg, 0, 0))
+    te = make_te(cfg, inputs.time_weights(cfg, 0))
+    pool.context_set(blk, 0, to_dev(inputs.context(cfg, 0, 0), torch.float32))
+    h = torch.zeros((cfg.tokens, cfg.hidden), dtype=torch.float32, device="cuda")
+    task = [runtime.make_task(0, 0, 0, 1.0, 0, [])]
+    streams = [torch.cuda.Stream() for _ in range(5)]
+    for st in streams[:4]:
+        runtime.stage_batch(pool, blk, te, task, h, h, cuda_stream=st)
+    torch.cuda.synchronize()
+    with pytest.raises(PsError) as ei:
+        runtime.stage_batch(pool, blk, te, task, h, h, cuda_stream=streams[4])
+    assert ei.value.status == PS_ERR_INVALID_ARG and "streams" in str(ei.value)
+    runtime.stage_batch(pool, blk, te, task, h, h, cuda_stream=streams[0])
+    torch.cuda.synchronize()
+    assert torch.isfinite(h).all()
+
+
 def test_invalid_arguments_rejected():
     cfg = C1
     pool = make_pool(cfg, n_streams=1, n_blocks=1)
