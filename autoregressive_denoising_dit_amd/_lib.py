@@ -23,6 +23,8 @@ STATUS_NAMES = {0: "PS_OK", -1: "PS_ERR_INVALID_ARG", -2: "PS_ERR_OUT_OF_MEMORY"
 
 PS_F32 = 0
 PS_BF16 = 1
+# ps_stage_kernel's kernels, in stage order
+KERNELS = ("ln1", "qkv", "attn_self", "o_proj", "ln2", "xq_proj", "attn_cross", "xo_proj", "ln3", "ffn1", "ffn2")
 PS_MAX_WINDOW = 8
 PS_MAX_TASKS = 32
 PS_FREQ_DIM = 256
@@ -34,7 +36,8 @@ EXPORTS = (
     "ps_euler_update", "ps_last_error", "ps_trace_enable", "ps_trace_collect", "ps_trace_count",
     "ps_trace_entry", "ps_head_create", "ps_head_destroy", "ps_patch_embed", "ps_output_head",
     "ps_sched_create", "ps_sched_destroy", "ps_sched_split", "ps_sched_admit", "ps_sched_release",
-    "ps_sched_gpu",
+    "ps_sched_gpu", "ps_kv_pool_release_stream", "ps_context_load", "ps_stage_kernel", "ps_timesteps",
+    "ps_euler_update_steps",
 )
 
 
@@ -125,6 +128,11 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ps_sched_admit": [vp, C.c_int64, C.POINTER(i32), i32, C.POINTER(i32)],
         "ps_sched_release": [vp, C.c_int64, C.POINTER(i32)],
         "ps_sched_gpu": [vp, i32, C.POINTER(i32), C.POINTER(C.c_double)],
+        "ps_kv_pool_release_stream": [vp, vp],
+        "ps_context_load": [vp, i32, i32, vp, vp, i32, vp],
+        "ps_stage_kernel": [vp, vp, vp, C.POINTER(Task), i32, i32, vp, vp, vp, vp],
+        "ps_timesteps": [i32, f32, C.POINTER(C.c_float)],
+        "ps_euler_update_steps": [vp, vp, C.POINTER(C.c_float), i32, C.POINTER(i32), i32, i32, i32, i32, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -6,12 +6,14 @@
 #include <string.h>
 
 #include <cstdarg>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
 
 #include "common.h"
 #include "kernels.h"
+#include "stage.h"
 
 using namespace ps;
 
@@ -46,33 +48,47 @@ namespace {
 
 size_t elt_size(ps_dtype t) { return t == PS_BF16 ? 2 : 4; }
 
-// A device buffer that grows on demand (old contents are not kept).
+// A device buffer that grows on demand (old contents are not kept).  Growth
+// is stream-ordered: the old buffer is freed and the new one allocated on the
+// stream whose calls use the buffer (hipFreeAsync / hipMallocAsync), so that
+// growing never waits for the device.  Where the device has no stream-ordered
+// allocator, the old buffer is freed after that stream alone has drained.
 struct DevBuf {
   void* p = nullptr;
   size_t bytes = 0;
-  ps_status reserve(size_t need) {
-    if (need <= bytes) return PS_OK;
-    if (p) {
-      // earlier launches may still read the old buffer
-      hipError_t e = hipDeviceSynchronize();
-      if (e != hipSuccess) return fail(PS_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+  bool async = false;   // p came from hipMallocAsync
+  void drop(hipStream_t s) {
+    if (!p) return;
+    if (async) {
+      (void)hipFreeAsync(p, s);
+    } else {
+      (void)hipStreamSynchronize(s);
       (void)hipFree(p);
-      p = nullptr;
-      bytes = 0;
     }
-    if (hipMalloc(&p, need) != hipSuccess) {
-      (void)hipGetLastError();
-      p = nullptr;
-      return fail(PS_ERR_OUT_OF_MEMORY, "workspace: cannot allocate %zu bytes", need);
-    }
-    bytes = need;
-    return PS_OK;
-  }
-  void release() {
-    if (p) (void)hipFree(p);
     p = nullptr;
     bytes = 0;
   }
+  ps_status reserve(size_t need, hipStream_t s) {
+    if (need <= bytes) return PS_OK;
+    drop(s);
+    void* q = nullptr;
+    hipError_t e = hipMallocAsync(&q, need, s);
+    if (e == hipSuccess) {
+      async = true;
+    } else {
+      (void)hipGetLastError();
+      async = false;
+      if (hipMalloc(&q, need) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(PS_ERR_OUT_OF_MEMORY, "workspace: cannot allocate %zu bytes", need);
+      }
+    }
+    p = q;
+    bytes = need;
+    return PS_OK;
+  }
+  // after all work that uses the buffer has completed
+  void release() { drop(nullptr); }
 };
 
 // ---------------------------------------------------------------- tracing
@@ -192,13 +208,7 @@ struct ps_kv_pool {
     hipStream_t stream = nullptr;
     DevBuf mod, rope, y, q, a, u, tasks;
     void release() {
-      mod.release();
-      rope.release();
-      y.release();
-      q.release();
-      a.release();
-      u.release();
-      tasks.release();
+      for (DevBuf* b : {&mod, &rope, &y, &q, &a, &u, &tasks}) b->release();
     }
   };
   std::vector<Workspace*> ws;
@@ -245,6 +255,11 @@ struct ps_block {
   ps_block_desc d{};
 };
 
+// Streams whose calls read rows of a timestep cache; each has an event that
+// is recorded after its latest read, so that a row is refilled only after
+// every read of its old contents (stream-ordered: no host wait).
+constexpr int TE_STREAMS = 16;
+
 struct ps_time_embed {
   ps_time_desc d{};
   float* cache = nullptr;      // [capacity][6][D]: e(t)
@@ -254,6 +269,15 @@ struct ps_time_embed {
   std::vector<uint64_t> used;
   std::vector<char> valid;
   uint64_t clock = 0;
+  std::vector<hipEvent_t> fill_ev;        // per row: recorded after its fill
+  std::vector<hipStream_t> fill_stream;   // per row: the stream of its fill
+  std::vector<uint32_t> readers;          // per row: stream slots that read it since its fill
+  hipStream_t rd_stream[TE_STREAMS] = {};
+  hipEvent_t rd_ev[TE_STREAMS] = {};
+  bool rd_used[TE_STREAMS] = {};
+  hipEvent_t scratch_ev = nullptr;        // recorded after the latest fill (the scratch is free)
+  hipStream_t scratch_stream = nullptr;
+  bool scratch_rec = false;
 };
 
 extern "C" const char* ps_last_error(void) { return g_err.c_str(); }
@@ -328,6 +352,19 @@ extern "C" ps_status ps_kv_pool_destroy(ps_kv_pool* p) {
   }
   p->ws.clear();
   delete p;
+  return PS_OK;
+}
+
+extern "C" ps_status ps_kv_pool_release_stream(ps_kv_pool* p, hipStream_t hs) {
+  if (!p) return fail(PS_ERR_INVALID_ARG, "ps_kv_pool_release_stream: null pool");
+  for (size_t i = 0; i < p->ws.size(); ++i) {
+    if (p->ws[i]->stream != hs) continue;
+    PS_HIP(hipStreamSynchronize(hs));
+    p->ws[i]->release();
+    delete p->ws[i];
+    p->ws.erase(p->ws.begin() + i);
+    return PS_OK;
+  }
   return PS_OK;
 }
 
@@ -427,6 +464,19 @@ extern "C" ps_status ps_block_destroy(ps_block* b) {
 }
 
 // ------------------------------------------------------ timestep embedding
+static void te_free(ps_time_embed* te) {
+  if (te->cache) (void)hipFree(te->cache);
+  if (te->cache_u) (void)hipFree(te->cache_u);
+  if (te->scratch) (void)hipFree(te->scratch);
+  for (hipEvent_t e : te->fill_ev)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : te->rd_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (te->scratch_ev) (void)hipEventDestroy(te->scratch_ev);
+  (void)hipGetLastError();
+  delete te;
+}
+
 extern "C" ps_status ps_time_embed_create(const ps_time_desc* desc, ps_time_embed** out) {
   if (!desc || !out) return fail(PS_ERR_INVALID_ARG, "ps_time_embed_create: null argument");
   const ps_time_desc& d = *desc;
@@ -436,18 +486,24 @@ extern "C" ps_status ps_time_embed_create(const ps_time_desc* desc, ps_time_embe
     return fail(PS_ERR_INVALID_ARG, "time embed: null weight pointer");
   ps_time_embed* te = new ps_time_embed();
   te->d = d;
-  if (hipMalloc(&te->cache, sizeof(float) * (size_t)d.capacity * 6 * d.hidden) != hipSuccess ||
-      hipMalloc(&te->cache_u, sizeof(float) * (size_t)d.capacity * d.hidden) != hipSuccess ||
-      hipMalloc(&te->scratch, sizeof(float) * (PS_FREQ_DIM + 2 * (size_t)d.hidden)) != hipSuccess) {
-    (void)hipGetLastError();
-    if (te->cache) (void)hipFree(te->cache);
-    if (te->cache_u) (void)hipFree(te->cache_u);
-    delete te;
-    return fail(PS_ERR_OUT_OF_MEMORY, "time embed: cannot allocate cache");
+  te->fill_ev.assign(d.capacity, nullptr);
+  bool ok = hipMalloc(&te->cache, sizeof(float) * (size_t)d.capacity * 6 * d.hidden) == hipSuccess &&
+            hipMalloc(&te->cache_u, sizeof(float) * (size_t)d.capacity * d.hidden) == hipSuccess &&
+            hipMalloc(&te->scratch, sizeof(float) * (PS_FREQ_DIM + 2 * (size_t)d.hidden)) == hipSuccess;
+  for (int i = 0; ok && i < d.capacity; ++i)
+    ok = hipEventCreateWithFlags(&te->fill_ev[i], hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; ok && i < TE_STREAMS; ++i)
+    ok = hipEventCreateWithFlags(&te->rd_ev[i], hipEventDisableTiming) == hipSuccess;
+  if (ok) ok = hipEventCreateWithFlags(&te->scratch_ev, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    te_free(te);
+    return fail(PS_ERR_OUT_OF_MEMORY, "time embed: cannot allocate the cache or its events");
   }
   te->key.assign(d.capacity, 0);
   te->used.assign(d.capacity, 0);
   te->valid.assign(d.capacity, 0);
+  te->fill_stream.assign(d.capacity, nullptr);
+  te->readers.assign(d.capacity, 0);
   *out = te;
   return PS_OK;
 }
@@ -455,58 +511,130 @@ extern "C" ps_status ps_time_embed_create(const ps_time_desc* desc, ps_time_embe
 extern "C" ps_status ps_time_embed_destroy(ps_time_embed* te) {
   if (!te) return fail(PS_ERR_INVALID_ARG, "ps_time_embed_destroy: null handle");
   (void)hipDeviceSynchronize();
-  (void)hipFree(te->cache);
-  (void)hipFree(te->cache_u);
-  (void)hipFree(te->scratch);
-  delete te;
+  te_free(te);
   return PS_OK;
 }
 
-// Row of e(t) in the cache, computing it if absent.  `pinned` rows (used by
-// the current batch) are never evicted.
-static ps_status te_row(ps_time_embed* te, float t, const std::vector<int>& pinned, hipStream_t hs, int* row) {
-  uint32_t k;
-  memcpy(&k, &t, 4);
-  const int cap = te->d.capacity;
-  for (int i = 0; i < cap; ++i)
-    if (te->valid[i] && te->key[i] == k) {
-      te->used[i] = ++te->clock;
-      *row = i;
+// Slot of stream hs among the streams that read the cache.  With all slots
+// taken, a slot whose latest read has completed is reused (its stream's bits
+// are cleared from every row); if none has, the host waits for the oldest
+// slot's latest read first.
+static ps_status te_stream_slot(ps_time_embed* te, hipStream_t hs, int* slot) {
+  for (int i = 0; i < TE_STREAMS; ++i)
+    if (te->rd_used[i] && te->rd_stream[i] == hs) {
+      *slot = i;
       return PS_OK;
     }
-  int victim = -1;
-  for (int i = 0; i < cap; ++i) {
-    bool pin = false;
-    for (int pr : pinned) pin |= (pr == i);
-    if (pin) continue;
-    if (victim < 0 || !te->valid[i] || (te->valid[victim] && te->used[i] < te->used[victim])) victim = i;
-    if (!te->valid[i]) break;
+  int pick = -1;
+  for (int i = 0; i < TE_STREAMS && pick < 0; ++i)
+    if (!te->rd_used[i]) pick = i;
+  for (int i = 0; i < TE_STREAMS && pick < 0; ++i)
+    if (hipEventQuery(te->rd_ev[i]) == hipSuccess) pick = i;
+  if (pick < 0) {
+    PS_HIP(hipEventSynchronize(te->rd_ev[0]));
+    pick = 0;
   }
-  if (victim < 0) return fail(PS_ERR_INVALID_ARG, "time embed: more distinct timesteps in one batch than capacity");
+  (void)hipGetLastError();   // hipEventQuery's hipErrorNotReady
+  for (uint32_t& r : te->readers) r &= ~(1u << pick);
+  te->rd_used[pick] = true;
+  te->rd_stream[pick] = hs;
+  *slot = pick;
+  return PS_OK;
+}
+
+// Cache rows of the timesteps t[0 .. n-1] (rows[i] for t[i]), filling the
+// missing ones on hs.  The number of distinct timesteps is checked against
+// the capacity before anything is enqueued.  A refilled row is first made to
+// wait for every earlier read of it on other streams, and a stream that reads
+// a row filled on another stream waits for that fill.  The rows of this call
+// are never evicted by it.
+static ps_status te_resolve(ps_time_embed* te, const float* t, int n, hipStream_t hs, int* rows, int* slot) {
+  const int cap = te->d.capacity;
+  std::vector<uint32_t> keys;
+  for (int i = 0; i < n; ++i) {
+    uint32_t k;
+    memcpy(&k, &t[i], 4);
+    bool seen = false;
+    for (uint32_t x : keys) seen |= (x == k);
+    if (!seen) keys.push_back(k);
+  }
+  if ((int)keys.size() > cap)
+    return fail(PS_ERR_INVALID_ARG, "time embed: %d distinct timesteps in one call, capacity %d", (int)keys.size(), cap);
+  ps_status st = te_stream_slot(te, hs, slot);
+  if (st) return st;
   const int D = te->d.hidden;
-  // A fill is rare (a new timestep).  It waits for all in-flight work, which
-  // may still read the victim row or use the scratch from another stream, and
-  // completes before the call returns, so that calls on any stream may read
-  // the row afterwards.
-  PS_HIP(hipDeviceSynchronize());
-  PS_HIP(launch_time_embed(t, te->d.wt1, te->d.bt1, te->d.wt2, te->d.bt2, te->d.wp, te->d.bp, D, te->scratch,
-                           te->cache + (size_t)victim * 6 * D, te->cache_u + (size_t)victim * D, hs));
-  PS_HIP(hipStreamSynchronize(hs));
-  te->valid[victim] = 1;
-  te->key[victim] = k;
-  te->used[victim] = ++te->clock;
-  *row = victim;
+  std::vector<int> pinned;
+  for (int i = 0; i < n; ++i) {
+    uint32_t k;
+    memcpy(&k, &t[i], 4);
+    int row = -1;
+    for (int j = 0; j < cap && row < 0; ++j)
+      if (te->valid[j] && te->key[j] == k) row = j;
+    if (row >= 0) {
+      if (te->fill_stream[row] != hs) PS_HIP(hipStreamWaitEvent(hs, te->fill_ev[row], 0));
+    } else {
+      int victim = -1;
+      for (int j = 0; j < cap; ++j) {
+        bool pin = false;
+        for (int pr : pinned) pin |= (pr == j);
+        if (pin) continue;
+        if (victim < 0 || !te->valid[j] || (te->valid[victim] && te->used[j] < te->used[victim])) victim = j;
+        if (!te->valid[j]) break;
+      }
+      // victim >= 0: at most `cap` distinct timesteps are pinned
+      for (int sl = 0; sl < TE_STREAMS; ++sl)
+        if ((te->readers[victim] >> sl & 1u) && te->rd_stream[sl] != hs)
+          PS_HIP(hipStreamWaitEvent(hs, te->rd_ev[sl], 0));
+      if (te->scratch_rec && te->scratch_stream != hs) PS_HIP(hipStreamWaitEvent(hs, te->scratch_ev, 0));
+      PS_HIP(launch_time_embed(t[i], te->d.wt1, te->d.bt1, te->d.wt2, te->d.bt2, te->d.wp, te->d.bp, D, te->scratch,
+                               te->cache + (size_t)victim * 6 * D, te->cache_u + (size_t)victim * D, hs));
+      PS_HIP(hipEventRecord(te->fill_ev[victim], hs));
+      PS_HIP(hipEventRecord(te->scratch_ev, hs));
+      te->scratch_rec = true;
+      te->scratch_stream = hs;
+      te->fill_stream[victim] = hs;
+      te->readers[victim] = 0;
+      te->valid[victim] = 1;
+      te->key[victim] = k;
+      row = victim;
+    }
+    te->used[row] = ++te->clock;
+    rows[i] = row;
+    pinned.push_back(row);
+  }
+  return PS_OK;
+}
+
+// After the kernels that read rows[0 .. n-1] have been enqueued on hs.
+static ps_status te_mark_read(ps_time_embed* te, const int* rows, int n, int slot, hipStream_t hs) {
+  PS_HIP(hipEventRecord(te->rd_ev[slot], hs));
+  for (int i = 0; i < n; ++i) te->readers[rows[i]] |= 1u << slot;
   return PS_OK;
 }
 
 extern "C" ps_status ps_time_embed_get(ps_time_embed* te, float t, float* e, hipStream_t hs) {
   if (!te || !e) return fail(PS_ERR_INVALID_ARG, "ps_time_embed_get: null argument");
   if (!isfinite(t)) return fail(PS_ERR_INVALID_ARG, "ps_time_embed_get: timestep not finite");
-  int row = 0;
-  ps_status st = te_row(te, t, {}, hs, &row);
+  int row = 0, slot = 0;
+  ps_status st = te_resolve(te, &t, 1, hs, &row, &slot);
   if (st) return st;
   const size_t n = (size_t)6 * te->d.hidden;
   PS_HIP(hipMemcpyAsync(e, te->cache + row * n, n * sizeof(float), hipMemcpyDeviceToDevice, hs));
+  return te_mark_read(te, &row, 1, slot, hs);
+}
+
+// Timesteps of an n_steps-step schedule: the uniform grid u = 1 - s / n_steps
+// under the flow-matching time shift t = a u / (1 + (a - 1) u) (a = shift;
+// a = 1 leaves the grid uniform), and t[n_steps] = 0.
+extern "C" ps_status ps_timesteps(int32_t n_steps, float shift, float* out) {
+  if (!out || n_steps < 1 || n_steps > 4096 || !(shift > 0.0f) || !isfinite(shift))
+    return fail(PS_ERR_INVALID_ARG, "ps_timesteps: need 1 <= n_steps <= 4096, a finite shift > 0 and out");
+  const double a = shift;
+  for (int s = 0; s < n_steps; ++s) {
+    const double u = 1.0 - (double)s / n_steps;
+    out[s] = (float)(a * u / (1.0 + (a - 1.0) * u));
+  }
+  out[n_steps] = 0.0f;
   return PS_OK;
 }
 
@@ -540,6 +668,27 @@ extern "C" ps_status ps_context_set(ps_kv_pool* p, const ps_block* b, int32_t st
   return PS_OK;
 }
 
+extern "C" ps_status ps_context_load(ps_kv_pool* p, int32_t stream, int32_t block, const void* k, const void* v,
+                                     int32_t n_ctx, hipStream_t hs) {
+  if (!p || !k || !v) return fail(PS_ERR_INVALID_ARG, "ps_context_load: null argument");
+  ps_status st = check_region(p, stream, block, 0, 0);
+  if (st) return st;
+  if (n_ctx < 8 || n_ctx > p->desc.max_ctx || n_ctx % 8 != 0)
+    return fail(PS_ERR_INVALID_ARG, "ps_context_load: n_ctx %d must be a multiple of 8 in [8, %d]", n_ctx,
+                p->desc.max_ctx);
+  const size_t cr = (size_t)stream * p->desc.n_blocks + block;
+  const size_t off = cr * p->ctx_elems;
+  const int H = p->desc.n_heads, d = p->desc.head_dim;
+  if (p->desc.dtype == PS_BF16)
+    PS_HIP(launch_entry_load<bf16>(static_cast<bf16*>(p->ctx) + off, static_cast<const bf16*>(k),
+                                   static_cast<const bf16*>(v), n_ctx, p->desc.max_ctx, H, d, hs));
+  else
+    PS_HIP(launch_entry_load<float>(static_cast<float*>(p->ctx) + off, static_cast<const float*>(k),
+                                    static_cast<const float*>(v), n_ctx, p->desc.max_ctx, H, d, hs));
+  p->ctx_len[cr] = n_ctx;
+  return PS_OK;
+}
+
 // ------------------------------------------------------------------ stage
 // Row stride of the activation buffers that feed a GEMM as its A operand:
 // padded by 64 elements so that the rows of a tile do not all begin on the
@@ -562,130 +711,49 @@ static ps_status probe_copy(void* dst, const void* src, size_t es, size_t rows, 
     }                                                                                              \
   } while (0)
 
-template <typename T>
-static ps_status run_stage(ps_kv_pool* p, ps_kv_pool::Workspace* w, const ps_block* b, const DevTask* tt, int n,
-                           const float* mod, const float2* rope_f, const float* h_in, float* h_out,
-                           const ps_stage_probe* pr, hipStream_t hs) {
-  const ps_block_desc& bd = b->d;
-  const int L = p->L(), D = bd.hidden, F = bd.ffn, M = n * L;
-  T* y = static_cast<T*>(w->y.p);
-  T* q = static_cast<T*>(w->q.p);
-  T* a = static_cast<T*>(w->a.p);
-  T* u = static_cast<T*>(w->u.p);
-  const PoolGeo pg = p->geo();
-  const float qscale = 1.4426950408889634f / sqrtf((float)bd.head_dim);
-  const T* W = nullptr;
-
-  // self-attention branch
-  const int ldy = act_ld(D), ldu = act_ld(F);
-  PS_TRACED("ln1", (launch_layernorm<T>(h_in, y, ldy, M, D, mod, 0, 1, L, hs)));
-  PS_PROBE(y1, y, D, ldy);
-  EpiArgs e1;
-  e1.bias = bd.bqkv;
-  e1.out = q;
-  e1.ldo = D;
-  e1.out_scale = qscale;
-  e1.rope_f = rope_f;
-  e1.pool = pg;
-  e1.d_shift = bd.head_dim == 128 ? 7 : 6;
-  W = static_cast<const T*>(bd.wqkv);
-  PS_TRACED("qkv", (launch_gemm<T>(EPI_QKV, y, ldy, W, M, 3 * D, D, e1, tt, hs)));
-  PS_PROBE(q, q, D, D);
-  PS_TRACED("attn_self", (launch_attention<T>(false, q, a, ldy, pg, tt, n, hs)));
-  PS_PROBE(attn, a, D, ldy);
-  EpiArgs e2;
-  e2.bias = bd.bo;
-  e2.h_in = h_in;
-  e2.h_out = h_out;
-  e2.mod = mod;
-  e2.gate_row = 2;
-  e2.L = L;
-  e2.div_L = FastDiv((uint32_t)L);
-  PS_TRACED("o_proj", (launch_gemm<T>(EPI_RES, a, ldy, static_cast<const T*>(bd.wo), M, D, D, e2, tt, hs)));
-  PS_PROBE(h1, h_out, D, D);
-
-  // cross-attention branch
-  PS_TRACED("ln2", (launch_layernorm<T>(h_out, y, ldy, M, D, nullptr, -1, -1, L, hs)));
-  PS_PROBE(y2, y, D, ldy);
-  EpiArgs e3;
-  e3.bias = bd.bq2;
-  e3.out = q;
-  e3.ldo = D;
-  e3.out_scale = qscale;
-  PS_TRACED("xq_proj", (launch_gemm<T>(EPI_STORE, y, ldy, static_cast<const T*>(bd.wq2), M, D, D, e3, tt, hs)));
-  PS_PROBE(q2, q, D, D);
-  PS_TRACED("attn_cross", (launch_attention<T>(true, q, a, ldy, pg, tt, n, hs)));
-  PS_PROBE(xattn, a, D, ldy);
-  EpiArgs e4;
-  e4.bias = bd.bo2;
-  e4.h_in = h_out;
-  e4.h_out = h_out;
-  e4.L = L;
-  e4.div_L = FastDiv((uint32_t)L);
-  PS_TRACED("xo_proj", (launch_gemm<T>(EPI_RES, a, ldy, static_cast<const T*>(bd.wo2), M, D, D, e4, tt, hs)));
-  PS_PROBE(h2, h_out, D, D);
-
-  // FFN branch
-  PS_TRACED("ln3", (launch_layernorm<T>(h_out, y, ldy, M, D, mod, 3, 4, L, hs)));
-  PS_PROBE(y3, y, D, ldy);
-  EpiArgs e5;
-  e5.bias = bd.b1;
-  e5.out = u;
-  e5.ldo = ldu;
-  PS_TRACED("ffn1", (launch_gemm<T>(EPI_GELU, y, ldy, static_cast<const T*>(bd.w1), M, F, D, e5, tt, hs)));
-  PS_PROBE(u, u, F, ldu);
-  EpiArgs e6;
-  e6.bias = bd.b2;
-  e6.h_in = h_out;
-  e6.h_out = h_out;
-  e6.mod = mod;
-  e6.gate_row = 5;
-  e6.L = L;
-  e6.div_L = FastDiv((uint32_t)L);
-  PS_TRACED("ffn2", (launch_gemm<T>(EPI_RES, u, ldu, static_cast<const T*>(bd.w2), M, D, F, e6, tt, hs)));
-  return PS_OK;
-}
-
-static ps_status stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const ps_task* tasks, int32_t n,
-                             const float* h_in, float* h_out, const ps_stage_probe* probe, hipStream_t hs) {
-  if (!p || !b || !te || !tasks || !h_in || !h_out) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: null argument");
-  if (n < 1 || n > PS_MAX_TASKS) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: n_tasks %d not in [1, %d]", n, PS_MAX_TASKS);
+// Every check of a stage call; nothing is enqueued or changed.
+ps_status ps::prepare_batch(const ps_kv_pool* p, const ps_block* b, const ps_time_embed* te, const ps_task* tasks,
+                               int32_t n, const void* h_in, const void* h_out, const char* fn, Batch* out) {
+  if (!p || !b || !te || !tasks || !h_in || !h_out) return fail(PS_ERR_INVALID_ARG, "%s: null argument", fn);
+  if (n < 1 || n > PS_MAX_TASKS) return fail(PS_ERR_INVALID_ARG, "%s: n_tasks %d not in [1, %d]", fn, n, PS_MAX_TASKS);
   const ps_pool_desc& pd = p->desc;
   const ps_block_desc& bd = b->d;
   if (bd.dtype != pd.dtype || bd.n_heads != pd.n_heads || bd.head_dim != pd.head_dim)
-    return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: block and pool disagree on dtype or heads");
-  if (bd.block_index >= pd.n_blocks) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: block_index %d beyond pool", bd.block_index);
-  if (te->d.hidden != bd.hidden) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: time embedding width differs");
+    return fail(PS_ERR_INVALID_ARG, "%s: block and pool disagree on dtype or heads", fn);
+  if (bd.block_index >= pd.n_blocks) return fail(PS_ERR_INVALID_ARG, "%s: block_index %d beyond pool", fn, bd.block_index);
+  if (te->d.hidden != bd.hidden) return fail(PS_ERR_INVALID_ARG, "%s: time embedding width differs", fn);
   int dev = 0;
   (void)hipGetDevice(&dev);
-  if (dev != p->device) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: current device is not the pool's");
+  if (dev != p->device) return fail(PS_ERR_INVALID_ARG, "%s: current device is not the pool's", fn);
 
-  TaskTable tt{};
-  tt.n = n;
-  std::vector<size_t> writes;
+  Batch& bt = *out;
+  bt.n = n;
+  bt.tt.n = n;
   for (int i = 0; i < n; ++i) {
     const ps_task& t = tasks[i];
     ps_status st = check_region(p, t.stream, bd.block_index, t.step, t.write_slot);
-    if (st) return fail(st, "task %d: %s", i, g_err.c_str());
-    if (t.chunk < 0) return fail(PS_ERR_INVALID_ARG, "task %d: negative chunk", i);
-    if (!isfinite(t.timestep)) return fail(PS_ERR_INVALID_ARG, "task %d: timestep not finite", i);
+    if (st) return fail(st, "%s: task %d: %s", fn, i, g_err.c_str());
+    if (t.chunk < 0) return fail(PS_ERR_INVALID_ARG, "%s: task %d: negative chunk", fn, i);
+    if (!isfinite(t.timestep)) return fail(PS_ERR_INVALID_ARG, "%s: task %d: timestep not finite", fn, i);
     if (t.n_read < 0 || t.n_read > PS_MAX_WINDOW || t.n_read >= pd.n_slots)
-      return fail(PS_ERR_INVALID_ARG, "task %d: n_read %d out of range", i, t.n_read);
+      return fail(PS_ERR_INVALID_ARG, "%s: task %d: n_read %d out of range", fn, i, t.n_read);
     for (int j = 0; j < t.n_read; ++j) {
       if (t.read_slots[j] < 0 || t.read_slots[j] >= pd.n_slots)
-        return fail(PS_ERR_INVALID_ARG, "task %d: read slot %d out of range", i, t.read_slots[j]);
+        return fail(PS_ERR_INVALID_ARG, "%s: task %d: read slot %d out of range", fn, i, t.read_slots[j]);
       if (t.read_slots[j] == t.write_slot)
-        return fail(PS_ERR_INVALID_ARG, "task %d: reads its own write slot %d", i, t.write_slot);
+        return fail(PS_ERR_INVALID_ARG, "%s: task %d: reads its own write slot %d", fn, i, t.write_slot);
     }
     const size_t cr = (size_t)t.stream * pd.n_blocks + bd.block_index;
     if (p->ctx_len[cr] == 0)
-      return fail(PS_ERR_INVALID_ARG, "task %d: context of stream %d block %d not set", i, t.stream, bd.block_index);
+      return fail(PS_ERR_INVALID_ARG, "%s: task %d: context of stream %d block %d not set", fn, i, t.stream,
+                  bd.block_index);
     const size_t reg = region_of(p, t.stream, bd.block_index, t.step);
     const size_t wkey = reg * pd.n_slots + t.write_slot;
-    for (size_t w : writes)
-      if (w == wkey) return fail(PS_ERR_SLOT_CONFLICT, "task %d: two tasks of the batch write one slot", i);
-    writes.push_back(wkey);
-    DevTask& dt = tt.t[i];
+    for (int j = 0; j < i; ++j)
+      if (bt.writes[j] == wkey) return fail(PS_ERR_SLOT_CONFLICT, "%s: task %d: two tasks of the batch write one slot", fn, i);
+    bt.writes[i] = wkey;
+    bt.t[i] = t.timestep;
+    DevTask& dt = bt.tt.t[i];
     dt.region = (int32_t)reg;
     dt.ctx_region = (int32_t)cr;
     dt.chunk = t.chunk;
@@ -697,53 +765,236 @@ static ps_status stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te
   if (pd.check_slots) {
     // the batch's writes land before any of its reads
     std::vector<int> led = p->ledger;
-    for (int i = 0; i < n; ++i) led[writes[i]] = tasks[i].chunk;
+    for (int i = 0; i < n; ++i) led[bt.writes[i]] = tasks[i].chunk;
     for (int i = 0; i < n; ++i) {
       const ps_task& t = tasks[i];
-      const size_t reg = tt.t[i].region;
+      const size_t reg = bt.tt.t[i].region;
       for (int j = 0; j < t.n_read; ++j) {
         const int want = t.chunk - t.n_read + j;
         const int have = led[reg * pd.n_slots + t.read_slots[j]];
         if (have != want)
-          return fail(PS_ERR_SLOT_CONFLICT, "task %d (stream %d chunk %d step %d): slot %d holds chunk %d, expected %d", i,
-                      t.stream, t.chunk, t.step, t.read_slots[j], have, want);
+          return fail(PS_ERR_SLOT_CONFLICT, "%s: task %d (stream %d chunk %d step %d): slot %d holds chunk %d, expected %d",
+                      fn, i, t.stream, t.chunk, t.step, t.read_slots[j], have, want);
       }
     }
   }
+  return PS_OK;
+}
 
-  // workspace
-  const int L = p->L(), D = bd.hidden, F = bd.ffn;
-  const size_t M = (size_t)n * L, es = elt_size(bd.dtype);
-  ps_status st;
+WsSizes ps::ws_sizes(const ps_kv_pool* p, const ps_block_desc& bd, int n) {
+  const size_t M = (size_t)n * p->L(), es = elt_size(bd.dtype);
+  const size_t D = bd.hidden, F = bd.ffn;
+  return WsSizes{{sizeof(float) * n * 6 * D, sizeof(float2) * n * p->desc.frames * (size_t)(p->seg_f / 2) + 16,
+                  M * act_ld((int)D) * es, M * D * es, M * act_ld((int)D) * es, M * act_ld((int)F) * es,
+                  sizeof(DevTask) * PS_MAX_TASKS}};
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t ps::ws_total(const WsSizes& z) {
+  size_t t = 0;
+  for (size_t v : z.b) t += align256(v);
+  return t;
+}
+
+WsPtrs ps::ws_carve(char* base, const WsSizes& z) {
+  void* p[7];
+  for (int i = 0; i < 7; ++i) {
+    p[i] = base;
+    base += align256(z.b[i]);
+  }
+  WsPtrs w;
+  w.mod = static_cast<float*>(p[0]);
+  w.rope = static_cast<float2*>(p[1]);
+  w.y = p[2];
+  w.q = p[3];
+  w.a = p[4];
+  w.u = p[5];
+  w.tasks = static_cast<DevTask*>(p[6]);
+  return w;
+}
+
+// The pool's per-stream workspace, grown to this batch (stream-ordered).
+static ps_status ws_from_pool(ps_kv_pool* p, const WsSizes& z, hipStream_t hs, WsPtrs* out) {
   ps_kv_pool::Workspace* w = p->workspace(hs);
   if (!w)
     return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: more than %d streams use this pool", PS_MAX_STREAMS_PER_POOL);
-  if ((st = w->mod.reserve(sizeof(float) * n * 6 * (size_t)D))) return st;
-  if ((st = w->rope.reserve(sizeof(float2) * n * pd.frames * (size_t)(p->seg_f / 2) + 16))) return st;
-  if ((st = w->y.reserve(M * act_ld(D) * es))) return st;
-  if ((st = w->q.reserve(M * D * es))) return st;
-  if ((st = w->a.reserve(M * act_ld(D) * es))) return st;
-  if ((st = w->u.reserve(M * act_ld(F) * es))) return st;
-  if ((st = w->tasks.reserve(sizeof(DevTask) * PS_MAX_TASKS))) return st;
-
-  // timestep embeddings (cached per distinct t)
-  std::vector<int> rows(n), pinned;
-  for (int i = 0; i < n; ++i) {
-    if ((st = te_row(te, tasks[i].timestep, pinned, hs, &rows[i]))) return st;
-    pinned.push_back(rows[i]);
+  DevBuf* bufs[7] = {&w->mod, &w->rope, &w->y, &w->q, &w->a, &w->u, &w->tasks};
+  for (int i = 0; i < 7; ++i) {
+    ps_status st = bufs[i]->reserve(z.b[i], hs);
+    if (st) return st;
   }
-  float* mod = static_cast<float*>(w->mod.p);
-  float2* rope_f = static_cast<float2*>(w->rope.p);
-  DevTask* dtasks = static_cast<DevTask*>(w->tasks.p);
-  PS_TRACED("put_tasks", launch_put_tasks(tt, dtasks, hs));
-  PS_TRACED("modulation", launch_modulation(te->cache, rows.data(), bd.tmod, mod, rope_f, dtasks, n, D, pd.frames, p->seg_f, hs));
+  out->mod = static_cast<float*>(w->mod.p);
+  out->rope = static_cast<float2*>(w->rope.p);
+  out->y = w->y.p;
+  out->q = w->q.p;
+  out->a = w->a.p;
+  out->u = w->u.p;
+  out->tasks = static_cast<DevTask*>(w->tasks.p);
+  return PS_OK;
+}
 
-  if (bd.dtype == PS_BF16)
-    st = run_stage<bf16>(p, w, b, dtasks, n, mod, rope_f, h_in, h_out, probe, hs);
-  else
-    st = run_stage<float>(p, w, b, dtasks, n, mod, rope_f, h_in, h_out, probe, hs);
+// The batch's preamble: timestep rows (filled if missing), the task table in
+// device memory, the per-task modulation rows and RoPE frame table.
+ps_status ps::begin_batch(const ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const Batch& bt,
+                             const WsPtrs& w, hipStream_t hs) {
+  int rows[PS_MAX_TASKS], slot = 0;
+  ps_status st = te_resolve(te, bt.t, bt.n, hs, rows, &slot);
   if (st) return st;
-  for (int i = 0; i < n; ++i) p->ledger[writes[i]] = tasks[i].chunk;
+  PS_TRACED("put_tasks", launch_put_tasks(bt.tt, w.tasks, hs));
+  PS_TRACED("modulation", launch_modulation(te->cache, rows, b->d.tmod, w.mod, w.rope, w.tasks, bt.n, b->d.hidden,
+                                            p->desc.frames, p->seg_f, hs));
+  return te_mark_read(te, rows, bt.n, slot, hs);
+}
+
+// The residual-stream buffers of the stage's steps: ln1 and the O projection
+// read h_in; the O projection writes h_out, which ln2, the cross-O projection
+// (in place), ln3 and FFN2 (in place) continue on.  A single-kernel call
+// points them at the caller's buffers.
+struct StageIO {
+  const float* h_in;     // ln1 input, O-projection residual input
+  float* h_out;          // O / cross-O / FFN2 output
+  const float* h_ln2;    // ln2 input
+  const float* h_xo;     // cross-O residual input
+  const float* h_ln3;    // ln3 input
+  const float* h_ffn2;   // FFN2 residual input
+};
+
+static StageIO stage_io(const float* h_in, float* h_out) {
+  return StageIO{h_in, h_out, h_out, h_out, h_out, h_out};
+}
+
+// The stage's kernels in order (which < 0), or the one kernel `which`.
+template <typename T>
+static ps_status run_stage(ps_kv_pool* p, const ps_block* b, const WsPtrs& w, int n, const StageIO& io,
+                           const ps_stage_probe* pr, int which, hipStream_t hs) {
+  const ps_block_desc& bd = b->d;
+  const int L = p->L(), D = bd.hidden, F = bd.ffn, M = n * L;
+  T* y = static_cast<T*>(w.y);
+  T* q = static_cast<T*>(w.q);
+  T* a = static_cast<T*>(w.a);
+  T* u = static_cast<T*>(w.u);
+  const DevTask* tt = w.tasks;
+  const PoolGeo pg = p->geo();
+  const float qscale = 1.4426950408889634f / sqrtf((float)bd.head_dim);
+  const int ldy = act_ld(D), ldu = act_ld(F);
+  auto on = [&](int k) { return which < 0 || which == k; };
+
+  // self-attention branch
+  if (on(PS_KERNEL_LN1)) {
+    PS_TRACED("ln1", (launch_layernorm<T>(io.h_in, y, ldy, M, D, w.mod, 0, 1, L, hs)));
+    PS_PROBE(y1, y, D, ldy);
+  }
+  if (on(PS_KERNEL_QKV)) {
+    EpiArgs e1;
+    e1.bias = bd.bqkv;
+    e1.out = q;
+    e1.ldo = D;
+    e1.out_scale = qscale;
+    e1.rope_f = w.rope;
+    e1.pool = pg;
+    e1.d_shift = bd.head_dim == 128 ? 7 : 6;
+    PS_TRACED("qkv", (launch_gemm<T>(EPI_QKV, y, ldy, static_cast<const T*>(bd.wqkv), M, 3 * D, D, e1, tt, hs)));
+    PS_PROBE(q, q, D, D);
+  }
+  if (on(PS_KERNEL_ATTN_SELF)) {
+    PS_TRACED("attn_self", (launch_attention<T>(false, q, a, ldy, pg, tt, n, hs)));
+    PS_PROBE(attn, a, D, ldy);
+  }
+  if (on(PS_KERNEL_O_PROJ)) {
+    EpiArgs e2;
+    e2.bias = bd.bo;
+    e2.h_in = io.h_in;
+    e2.h_out = io.h_out;
+    e2.mod = w.mod;
+    e2.gate_row = 2;
+    e2.L = L;
+    e2.div_L = FastDiv((uint32_t)L);
+    PS_TRACED("o_proj", (launch_gemm<T>(EPI_RES, a, ldy, static_cast<const T*>(bd.wo), M, D, D, e2, tt, hs)));
+    PS_PROBE(h1, io.h_out, D, D);
+  }
+
+  // cross-attention branch
+  if (on(PS_KERNEL_LN2)) {
+    PS_TRACED("ln2", (launch_layernorm<T>(io.h_ln2, y, ldy, M, D, nullptr, -1, -1, L, hs)));
+    PS_PROBE(y2, y, D, ldy);
+  }
+  if (on(PS_KERNEL_XQ_PROJ)) {
+    EpiArgs e3;
+    e3.bias = bd.bq2;
+    e3.out = q;
+    e3.ldo = D;
+    e3.out_scale = qscale;
+    PS_TRACED("xq_proj", (launch_gemm<T>(EPI_STORE, y, ldy, static_cast<const T*>(bd.wq2), M, D, D, e3, tt, hs)));
+    PS_PROBE(q2, q, D, D);
+  }
+  if (on(PS_KERNEL_ATTN_CROSS)) {
+    PS_TRACED("attn_cross", (launch_attention<T>(true, q, a, ldy, pg, tt, n, hs)));
+    PS_PROBE(xattn, a, D, ldy);
+  }
+  if (on(PS_KERNEL_XO_PROJ)) {
+    EpiArgs e4;
+    e4.bias = bd.bo2;
+    e4.h_in = io.h_xo;
+    e4.h_out = io.h_out;
+    e4.L = L;
+    e4.div_L = FastDiv((uint32_t)L);
+    PS_TRACED("xo_proj", (launch_gemm<T>(EPI_RES, a, ldy, static_cast<const T*>(bd.wo2), M, D, D, e4, tt, hs)));
+    PS_PROBE(h2, io.h_out, D, D);
+  }
+
+  // FFN branch
+  if (on(PS_KERNEL_LN3)) {
+    PS_TRACED("ln3", (launch_layernorm<T>(io.h_ln3, y, ldy, M, D, w.mod, 3, 4, L, hs)));
+    PS_PROBE(y3, y, D, ldy);
+  }
+  if (on(PS_KERNEL_FFN1)) {
+    EpiArgs e5;
+    e5.bias = bd.b1;
+    e5.out = u;
+    e5.ldo = ldu;
+    PS_TRACED("ffn1", (launch_gemm<T>(EPI_GELU, y, ldy, static_cast<const T*>(bd.w1), M, F, D, e5, tt, hs)));
+    PS_PROBE(u, u, F, ldu);
+  }
+  if (on(PS_KERNEL_FFN2)) {
+    EpiArgs e6;
+    e6.bias = bd.b2;
+    e6.h_in = io.h_ffn2;
+    e6.h_out = io.h_out;
+    e6.mod = w.mod;
+    e6.gate_row = 5;
+    e6.L = L;
+    e6.div_L = FastDiv((uint32_t)L);
+    PS_TRACED("ffn2", (launch_gemm<T>(EPI_RES, u, ldu, static_cast<const T*>(bd.w2), M, D, F, e6, tt, hs)));
+  }
+  return PS_OK;
+}
+
+static ps_status run_stage_dt(ps_kv_pool* p, const ps_block* b, const WsPtrs& w, int n, const StageIO& io,
+                              const ps_stage_probe* pr, int which, hipStream_t hs) {
+  if (b->d.dtype == PS_BF16) return run_stage<bf16>(p, b, w, n, io, pr, which, hs);
+  return run_stage<float>(p, b, w, n, io, pr, which, hs);
+}
+
+ps_status ps::run_stage_all(ps_kv_pool* p, const ps_block* b, const WsPtrs& w, int n, const float* h_in,
+                            float* h_out, hipStream_t hs) {
+  return run_stage_dt(p, b, w, n, stage_io(h_in, h_out), nullptr, -1, hs);
+}
+
+void ps::commit_writes(ps_kv_pool* p, const Batch& bt, const ps_task* tasks) {
+  for (int i = 0; i < bt.n; ++i) p->ledger[bt.writes[i]] = tasks[i].chunk;
+}
+
+static ps_status stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const ps_task* tasks, int32_t n,
+                             const float* h_in, float* h_out, const ps_stage_probe* probe, hipStream_t hs) {
+  Batch bt;
+  ps_status st = prepare_batch(p, b, te, tasks, n, h_in, h_out, "ps_stage_batch", &bt);
+  if (st) return st;
+  WsPtrs w;
+  if ((st = ws_from_pool(p, ws_sizes(p, b->d, n), hs, &w))) return st;
+  if ((st = begin_batch(p, b, te, bt, w, hs))) return st;
+  if ((st = run_stage_dt(p, b, w, n, stage_io(h_in, h_out), probe, -1, hs))) return st;
+  commit_writes(p, bt, tasks);
   return PS_OK;
 }
 
@@ -757,6 +1008,53 @@ extern "C" ps_status ps_stage_batch_probe(ps_kv_pool* p, const ps_block* b, ps_t
                                           const ps_stage_probe* probe, hipStream_t hs) {
   if (!probe) return fail(PS_ERR_INVALID_ARG, "ps_stage_batch_probe: null probe");
   return stage_batch(p, b, te, tasks, n, h_in, h_out, probe, hs);
+}
+
+// One kernel of the stage on caller-given inputs (dense rows).  The input is
+// copied into the workspace buffer the kernel reads in a stage call (same
+// strides), the kernel runs with the stage call's launch configuration, and
+// its output is copied out.
+extern "C" ps_status ps_stage_kernel(ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const ps_task* tasks,
+                                     int32_t n, int32_t kernel, const void* in, const float* h_in, void* out,
+                                     hipStream_t hs) {
+  const char* fn = "ps_stage_kernel";
+  if (kernel < PS_KERNEL_LN1 || kernel > PS_KERNEL_FFN2) return fail(PS_ERR_INVALID_ARG, "%s: unknown kernel %d", fn, kernel);
+  const bool residual = kernel == PS_KERNEL_O_PROJ || kernel == PS_KERNEL_XO_PROJ || kernel == PS_KERNEL_FFN2;
+  if (residual && !h_in) return fail(PS_ERR_INVALID_ARG, "%s: the residual kernels need h_in", fn);
+  Batch bt;
+  ps_status st = prepare_batch(p, b, te, tasks, n, in, out, fn, &bt);
+  if (st) return st;
+  WsPtrs w;
+  if ((st = ws_from_pool(p, ws_sizes(p, b->d, n), hs, &w))) return st;
+  if ((st = begin_batch(p, b, te, bt, w, hs))) return st;
+  const int L = p->L(), D = b->d.hidden, F = b->d.ffn;
+  const size_t M = (size_t)n * L, es = elt_size(b->d.dtype);
+  const int ldy = act_ld(D), ldu = act_ld(F);
+  auto put = [&](void* dst, int cols, int ld) -> ps_status {
+    PS_HIP(hipMemcpy2DAsync(dst, ld * es, in, cols * es, cols * es, M, hipMemcpyDeviceToDevice, hs));
+    return PS_OK;
+  };
+  StageIO io = stage_io(static_cast<const float*>(in), static_cast<float*>(out));
+  const void* res = nullptr;   // workspace output to copy out
+  int res_cols = D, res_ld = ldy;
+  switch (kernel) {
+    case PS_KERNEL_LN1: res = w.y; break;
+    case PS_KERNEL_QKV: st = put(w.y, D, ldy); res = w.q; res_ld = D; break;
+    case PS_KERNEL_ATTN_SELF: st = put(w.q, D, D); res = w.a; break;
+    case PS_KERNEL_O_PROJ: st = put(w.a, D, ldy); io.h_in = h_in; break;
+    case PS_KERNEL_LN2: io.h_ln2 = static_cast<const float*>(in); res = w.y; break;
+    case PS_KERNEL_XQ_PROJ: st = put(w.y, D, ldy); res = w.q; res_ld = D; break;
+    case PS_KERNEL_ATTN_CROSS: st = put(w.q, D, D); res = w.a; break;
+    case PS_KERNEL_XO_PROJ: st = put(w.a, D, ldy); io.h_xo = h_in; break;
+    case PS_KERNEL_LN3: io.h_ln3 = static_cast<const float*>(in); res = w.y; break;
+    case PS_KERNEL_FFN1: st = put(w.y, D, ldy); res = w.u; res_cols = F; res_ld = ldu; break;
+    case PS_KERNEL_FFN2: st = put(w.u, F, ldu); io.h_ffn2 = h_in; break;
+  }
+  if (st) return st;
+  if ((st = run_stage_dt(p, b, w, n, io, nullptr, kernel, hs))) return st;
+  if (res) PS_HIP(hipMemcpy2DAsync(out, res_cols * es, res, res_ld * es, res_cols * es, M, hipMemcpyDeviceToDevice, hs));
+  if (kernel == PS_KERNEL_QKV) commit_writes(p, bt, tasks);
+  return PS_OK;
 }
 
 // ------------------------------------------------------------------- head
@@ -814,7 +1112,7 @@ extern "C" ps_status ps_patch_embed(ps_head* h, const float* x, float* out, int3
   ep.out = out;
   ep.ldo = d.hidden;
   if (d.dtype == PS_BF16) {
-    if ((st = h->ws_x.reserve(n * sizeof(bf16)))) return st;
+    if ((st = h->ws_x.reserve(n * sizeof(bf16), hs))) return st;
     bf16* xb = static_cast<bf16*>(h->ws_x.p);
     PS_TRACED("embed_cast", launch_cast<bf16>(x, xb, n, hs));
     PS_TRACED("embed", (launch_gemm<bf16>(EPI_F32, xb, d.latent_dim, static_cast<const bf16*>(d.w_embed), n_rows,
@@ -854,15 +1152,13 @@ extern "C" ps_status ps_output_head(ps_head* hd, ps_time_embed* te, const float*
     if (!isfinite(t[i])) return fail(PS_ERR_INVALID_ARG, "ps_output_head: t[%d] not finite", i);
   const size_t M = (size_t)n * tokens;
   if (M > (size_t)INT32_MAX / 2) return fail(PS_ERR_INVALID_ARG, "ps_output_head: too many rows");
-  if ((st = hd->ws_y.reserve(M * act_ld(d.hidden) * elt_size(d.dtype)))) return st;
-  if ((st = hd->ws_mod.reserve(sizeof(float) * (size_t)n * 6 * d.hidden))) return st;
-  std::vector<int> rows(n), pinned;
-  for (int i = 0; i < n; ++i) {
-    if ((st = te_row(te, t[i], pinned, hs, &rows[i]))) return st;
-    pinned.push_back(rows[i]);
-  }
+  if ((st = hd->ws_y.reserve(M * act_ld(d.hidden) * elt_size(d.dtype), hs))) return st;
+  if ((st = hd->ws_mod.reserve(sizeof(float) * (size_t)n * 6 * d.hidden, hs))) return st;
+  int rows[PS_MAX_TASKS], slot = 0;
+  if ((st = te_resolve(te, t, n, hs, rows, &slot))) return st;
   float* mod = static_cast<float*>(hd->ws_mod.p);
-  PS_TRACED("head_mod", launch_head_mod(te->cache_u, rows.data(), d.t_head, mod, n, d.hidden, hs));
+  PS_TRACED("head_mod", launch_head_mod(te->cache_u, rows, d.t_head, mod, n, d.hidden, hs));
+  if ((st = te_mark_read(te, rows, n, slot, hs))) return st;
   if (d.dtype == PS_BF16) return run_head<bf16>(hd, h, v, (int)M, tokens, mod, hs);
   return run_head<float>(hd, h, v, (int)M, tokens, mod, hs);
 }
@@ -881,4 +1177,20 @@ extern "C" ps_status ps_euler_update(float* x, const void* v, const float* dt, i
     return fail(PS_ERR_INVALID_ARG, "ps_euler_update: x and v must be 16-byte aligned");
   PS_TRACED("euler", launch_euler(x, v, v_dtype, dt, n, tokens, hidden, hs));
   return PS_OK;
+}
+
+extern "C" ps_status ps_euler_update_steps(float* x, const void* v, const float* timesteps, int32_t n_steps,
+                                           const int32_t* steps, int32_t n, int32_t tokens, int32_t hidden,
+                                           ps_dtype v_dtype, hipStream_t hs) {
+  if (!timesteps || !steps) return fail(PS_ERR_INVALID_ARG, "ps_euler_update_steps: null argument");
+  if (n < 1 || n > PS_MAX_TASKS) return fail(PS_ERR_INVALID_ARG, "ps_euler_update_steps: n_tasks %d not in [1, %d]", n, PS_MAX_TASKS);
+  if (n_steps < 1) return fail(PS_ERR_INVALID_ARG, "ps_euler_update_steps: n_steps %d must be positive", n_steps);
+  float dt[PS_MAX_TASKS];
+  for (int i = 0; i < n; ++i) {
+    const int s = steps[i];
+    if (s < 0 || s >= n_steps) return fail(PS_ERR_INVALID_ARG, "ps_euler_update_steps: step %d of task %d out of range", s, i);
+    const float next = s + 1 < n_steps ? timesteps[s + 1] : 0.0f;
+    dt[i] = timesteps[s] - next;
+  }
+  return ps_euler_update(x, v, dt, n, tokens, hidden, v_dtype, hs);
 }

@@ -90,6 +90,18 @@ class Pool:
                                         _stream_ptr(cuda_stream)))
         return k, v
 
+    def context_load(self, stream: int, block: int, k: torch.Tensor, v: torch.Tensor, cuda_stream=None):
+        """Stores given cross-attention keys/values [n_ctx, H, d] of (stream, block)."""
+        td = TORCH_DTYPE[self.dtype]
+        n = k.shape[0]
+        _need(k, td, self._kv_shape(n), "k")
+        _need(v, td, self._kv_shape(n), "v")
+        check(self.lib.ps_context_load(self.handle, stream, block, _ptr(k), _ptr(v), n, _stream_ptr(cuda_stream)))
+
+    def release_stream(self, cuda_stream) -> None:
+        """Waits for the stream and frees the workspace the pool keeps for it."""
+        check(self.lib.ps_kv_pool_release_stream(self.handle, _stream_ptr(cuda_stream)))
+
     def context_set(self, block: "Block", stream: int, ctx: torch.Tensor, cuda_stream=None):
         _need(ctx, TORCH_DTYPE[self.dtype], (ctx.shape[0], self.hidden), "ctx")
         check(self.lib.ps_context_set(self.handle, block.handle, stream, _ptr(ctx), ctx.shape[0],
@@ -295,6 +307,51 @@ def stage_batch_probe(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task]
     arr = (Task * max(n, 1))(*tasks)
     check(pool.lib.ps_stage_batch_probe(pool.handle, block.handle, te.handle, arr, n, _ptr(h_in), _ptr(h_out),
                                         C.byref(pr), _stream_ptr(cuda_stream)))
+
+
+def stage_kernel(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], kernel: str, x: torch.Tensor,
+                 out: torch.Tensor, h_in: Optional[torch.Tensor] = None, cuda_stream=None) -> None:
+    """One kernel of the stage (_lib.KERNELS) on the given input x; see
+    ps_stage_kernel for each kernel's input, residual input and output."""
+    n = len(tasks)
+    M, D, F = n * pool.tokens, pool.hidden, block.ffn
+    td = TORCH_DTYPE[block.dtype]
+    k = _lib.KERNELS.index(kernel)
+    fp_in = kernel in ("ln1", "ln2", "ln3")
+    fp_out = kernel in ("o_proj", "xo_proj", "ffn2")
+    _need(x, torch.float32 if fp_in else td, (M, F if kernel == "ffn2" else D), "x")
+    _need(out, torch.float32 if fp_out else td, (M, F if kernel == "ffn1" else D), "out")
+    if fp_out:
+        if h_in is None:
+            raise ValueError(f"{kernel} needs h_in")
+        _need(h_in, torch.float32, (M, D), "h_in")
+    arr = (Task * max(n, 1))(*tasks)
+    check(pool.lib.ps_stage_kernel(pool.handle, block.handle, te.handle, arr, n, k, _ptr(x), _ptr(h_in), _ptr(out),
+                                   _stream_ptr(cuda_stream)))
+
+
+def timesteps(n_steps: int, shift: float = 1.0) -> List[float]:
+    """t_0 .. t_{S-1} of an S-step schedule under the flow-matching time shift
+    (ps_timesteps; the list leaves out t_S = 0)."""
+    out = (C.c_float * (n_steps + 1))()
+    check(_lib.load().ps_timesteps(n_steps, C.c_float(shift), out))
+    return [float(out[i]) for i in range(n_steps)]
+
+
+def euler_update_steps(x: torch.Tensor, v: torch.Tensor, ts: Sequence[float], steps: Sequence[int], tokens: int,
+                       hidden: int, cuda_stream=None) -> None:
+    """Euler step of each task with dt taken from the schedule ts (t_S = 0) at
+    the task's step (ps_euler_update_steps)."""
+    n = len(steps)
+    _need(x, torch.float32, (n * tokens, hidden), "x")
+    if v.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("v must be fp32 or bf16")
+    _need(v, v.dtype, (n * tokens, hidden), "v")
+    vdt = PS_F32 if v.dtype == torch.float32 else PS_BF16
+    tarr = (C.c_float * len(ts))(*[float(t) for t in ts])
+    sarr = (C.c_int32 * n)(*[int(s) for s in steps])
+    check(_lib.load().ps_euler_update_steps(_ptr(x), _ptr(v), tarr, len(ts), sarr, n, tokens, hidden, vdt,
+                                            _stream_ptr(cuda_stream)))
 
 
 def euler_update(x: torch.Tensor, v: torch.Tensor, dt: Sequence[float], tokens: int, hidden: int,

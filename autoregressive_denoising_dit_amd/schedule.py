@@ -36,12 +36,13 @@ from .runtime import Block, Head, Pool, TimeEmbed
 
 def shifted_timesteps(n_steps: int, shift: float = 1.0) -> Tuple[float, ...]:
     """Timesteps t_0 > ... > t_{S-1} (t_S = 0): the uniform grid u = 1 - s/S
-    under the flow-matching time shift t = a u / (1 + (a - 1) u), a = shift.
-    a = 1 is the uniform schedule; a > 1 spends more of the steps at high
-    noise.  The pages fix four steps but no values."""
+    under the flow-matching time shift t = a u / (1 + (a - 1) u), a = shift,
+    computed by the library (ps_timesteps).  a = 1 is the uniform schedule;
+    a > 1 spends more of the steps at high noise.  The pages fix four steps
+    but no values."""
     if n_steps < 1 or not shift > 0:
         raise ValueError("need n_steps >= 1 and shift > 0")
-    return tuple(shift * (1.0 - s / n_steps) / (1.0 + (shift - 1.0) * (1.0 - s / n_steps)) for s in range(n_steps))
+    return tuple(runtime.timesteps(n_steps, shift))
 
 
 def tick_tasks(tau: int, n_chunks: int, n_steps: int, k: int, n_streams: int) -> List[Tuple[int, int, int]]:
@@ -104,13 +105,13 @@ class StaggeredRunner:
             runtime.patch_embed(self.head, xs, h)
         for b, blk in enumerate(self.blocks):
             runtime.stage_batch(self.pool, blk, self.te, tasks, xs if (b == 0 and self.head is None) else h, h)
-        dts = [self.ts[s] - self.ts[s + 1] for (_, _, s) in tl]
+        steps = [s for (_, _, s) in tl]
         if self.head is not None:
             v = self.vbuf[:rows]
-            runtime.output_head(self.head, self.te, [self.ts[s] for (_, _, s) in tl], self.L, h, v)
-            runtime.euler_update(xs, v, dts, self.L, self.P)
+            runtime.output_head(self.head, self.te, [self.ts[s] for s in steps], self.L, h, v)
+            runtime.euler_update_steps(xs, v, self.ts[:-1], steps, self.L, self.P)
         else:
-            runtime.euler_update(xs, h, dts, self.L, self.D)
+            runtime.euler_update_steps(xs, h, self.ts[:-1], steps, self.L, self.D)
         return tl
 
     def run(self, x: torch.Tensor, n_chunks: int, on_tick: Optional[Callable[[int, list], None]] = None):

@@ -15,7 +15,8 @@
  *
  * Conventions for every call.
  *  - Return value: PS_OK (0) or a negative ps_status.  On failure nothing has
- *    been enqueued on the stream and ps_last_error() holds a message.
+ *    been enqueued on the stream (see below) and ps_last_error() holds a
+ *    message.
  *  - Arguments are validated on the host before any launch.  Calls that take a
  *    hipStream_t are asynchronous in that stream's order; a device fault shows
  *    up as PS_ERR_HIP on a later call.
@@ -29,7 +30,13 @@
  *    the pool), provided no batch reads or writes a KV slot that a concurrent
  *    batch writes; all other calls that share a handle are ordered on one
  *    stream.  Filling a timestep-embedding cache row (a timestep not cached)
- *    waits for all device work and completes before the call returns.
+ *    is stream-ordered: the fill waits on the device for the earlier reads of
+ *    the row it replaces, and a call on another stream that reads the row
+ *    waits on the device for the fill.  No call waits on the host, except
+ *    the *_destroy calls, ps_kv_pool_release_stream and ps_trace_enable.
+ *  - A failing call enqueues nothing, with one exception: a HIP runtime
+ *    failure part-way through a call's launches (PS_ERR_HIP) may leave the
+ *    launches before it enqueued.
  *  - Element types: ps_dtype PS_BF16 (bfloat16) or PS_F32.  "compute dtype"
  *    means the dtype of the pool/block.  The residual stream (h) and the
  *    latents (x) are always fp32; biases, modulation tables and the timestep
@@ -99,6 +106,10 @@ typedef struct {
  * Errors: PS_ERR_INVALID_ARG (bad sizes), PS_ERR_OUT_OF_MEMORY, PS_ERR_HIP. */
 ps_status ps_kv_pool_create(const ps_pool_desc* desc, ps_kv_pool** out);
 ps_status ps_kv_pool_destroy(ps_kv_pool* pool);
+/* Waits for the work on hs and frees the workspace the pool keeps for calls
+ * on hs (one of the PS_MAX_STREAMS_PER_POOL), so that another stream may take
+ * its place.  A stream the pool has no workspace for is a no-op. */
+ps_status ps_kv_pool_release_stream(ps_kv_pool* pool, hipStream_t hs);
 
 /* Copies one chunk's cache entry into a slot, or out of it.
  * k, v: device, [L, n_heads, head_dim] row-major in the compute dtype (k after
@@ -115,6 +126,14 @@ ps_status ps_context_fetch(const ps_kv_pool* pool, int32_t stream, int32_t block
                            void* k, void* v, hipStream_t hs);
 
 /* ----------------------------------------------------------------- block --
+ * A block's weights are shared by all its stages -- the block at every
+ * denoising step -- which is what lets a GPU batch a block's tasks of
+ * different chunks and steps against one copy of them (AREX article,
+ * "三层设计", layer 2; aicoder news, "Time-Shared Multi-Request Batching":
+ * heterogeneous denoising stages on one block).  The layout of the block is
+ * that of the Wan-family backbones the pages evaluate (AREX article,
+ * "实测数字"): AdaLN-modulated self-attention with a gate, cross-attention to
+ * conditioning tokens, AdaLN-modulated GELU-tanh FFN with a gate.
  * One DiT block's weights, borrowed (device pointers, kept until
  * ps_block_destroy).  Linear weights are [out, in] row-major in the compute
  * dtype (y = x W^T + b).  With D = hidden, F = ffn:
@@ -140,6 +159,10 @@ ps_status ps_block_create(const ps_block_desc* desc, ps_block** out);
 ps_status ps_block_destroy(ps_block* block);
 
 /* ------------------------------------------------------ timestep embedding --
+ * Tasks of one batch sit at different denoising steps, so each carries its
+ * own timestep and modulation (AREX article, "三层设计", layer 2: tasks of
+ * different chunks and denoising steps on one block).  Wan-style 6-way
+ * modulation from a timestep embedding:
  * e(t) in R^{6 x D}, shared by all blocks:
  *   phi(t) = [cos(1000 t w_j) | sin(1000 t w_j)], w_j = 10000^(-j/128), j < 128
  *   u = SiLU(phi wt1^T + bt1) wt2^T + bt2;  e = SiLU(u) wp^T + bp.
@@ -158,6 +181,13 @@ ps_status ps_time_embed_destroy(ps_time_embed* te);
 /* Writes e(t) (fp32 [6, D], device) -- computes it if not cached. */
 ps_status ps_time_embed_get(ps_time_embed* te, float t, float* e, hipStream_t hs);
 
+/* Timesteps of a schedule of n_steps denoising steps (the pages run four
+ * steps per chunk -- AREX article, "实测数字" -- and give no values): the
+ * uniform grid u = 1 - s / n_steps under the flow-matching time shift
+ * t = a u / (1 + (a - 1) u), a = shift > 0 (a = 1 leaves it uniform).
+ * out: host float [n_steps + 1], out[n_steps] = 0.  Host only. */
+ps_status ps_timesteps(int32_t n_steps, float shift, float* out);
+
 /* --------------------------------------------------------------- context --
  * Computes and caches the cross-attention keys/values of one stream's
  * conditioning tokens for one block: k2 = ctx wkv2[:D]^T + bkv2[:D],
@@ -166,6 +196,10 @@ ps_status ps_time_embed_get(ps_time_embed* te, float t, float* e, hipStream_t hs
  * whose tasks belong to that stream. */
 ps_status ps_context_set(ps_kv_pool* pool, const ps_block* block, int32_t stream,
                          const void* ctx, int32_t n_ctx, hipStream_t hs);
+/* Stores given cross-attention keys/values of (stream, block) instead:
+ * k, v device [n_ctx, n_heads, head_dim], compute dtype; n_ctx as above. */
+ps_status ps_context_load(ps_kv_pool* pool, int32_t stream, int32_t block, const void* k,
+                          const void* v, int32_t n_ctx, hipStream_t hs);
 
 /* ----------------------------------------------------------------- stage --
  * One stage task (host struct).  The task runs `block` at `step` for chunk
@@ -238,6 +272,44 @@ ps_status ps_stage_batch_probe(ps_kv_pool* pool, const ps_block* block, ps_time_
                                const ps_task* tasks, int32_t n_tasks, const float* h_in,
                                float* h_out, const ps_stage_probe* probe, hipStream_t hs);
 
+/* One kernel of the stage on caller-given inputs, for checking each kernel
+ * on identical inputs (the stage's steps are those of ps_stage_batch).  The
+ * call does the batch's preamble (validation, timestep rows, modulation rows),
+ * then runs kernel `kernel` with the launch configuration of ps_stage_batch:
+ *   kernel               in (device, dense)        h_in          out (device, dense)
+ *   PS_KERNEL_LN1        h fp32 [n*L, D]           -             y1 dt [n*L, D]
+ *   PS_KERNEL_QKV        y1 dt [n*L, D]            -             q dt [n*L, D] (*)
+ *   PS_KERNEL_ATTN_SELF  q dt [n*L, D] (*)         -             attn dt [n*L, D]
+ *   PS_KERNEL_O_PROJ     attn dt [n*L, D]          h fp32        h1 fp32 [n*L, D]
+ *   PS_KERNEL_LN2        h1 fp32                   -             y2 dt
+ *   PS_KERNEL_XQ_PROJ    y2 dt                     -             q2 dt (*)
+ *   PS_KERNEL_ATTN_CROSS q2 dt (*)                 -             xattn dt
+ *   PS_KERNEL_XO_PROJ    xattn dt                  h1 fp32       h2 fp32
+ *   PS_KERNEL_LN3        h2 fp32                   -             y3 dt
+ *   PS_KERNEL_FFN1       y3 dt                     -             u dt [n*L, F]
+ *   PS_KERNEL_FFN2       u dt [n*L, F]             h2 fp32       h_out fp32
+ * (*) queries multiplied by log2(e)/sqrt(head_dim).  PS_KERNEL_QKV also
+ * writes each task's keys/values into its write slot (and the slot ledger);
+ * PS_KERNEL_ATTN_SELF reads the window's slots (ps_kv_pool_load fills them),
+ * PS_KERNEL_ATTN_CROSS the (stream, block) context entry (ps_context_load).
+ * h_in is required by the three residual kernels and ignored otherwise.
+ * Errors as ps_stage_batch, plus PS_ERR_INVALID_ARG for an unknown kernel.
+ * For tests: it copies its input and output, so it is not a fast path. */
+#define PS_KERNEL_LN1 0
+#define PS_KERNEL_QKV 1
+#define PS_KERNEL_ATTN_SELF 2
+#define PS_KERNEL_O_PROJ 3
+#define PS_KERNEL_LN2 4
+#define PS_KERNEL_XQ_PROJ 5
+#define PS_KERNEL_ATTN_CROSS 6
+#define PS_KERNEL_XO_PROJ 7
+#define PS_KERNEL_LN3 8
+#define PS_KERNEL_FFN1 9
+#define PS_KERNEL_FFN2 10
+ps_status ps_stage_kernel(ps_kv_pool* pool, const ps_block* block, ps_time_embed* te,
+                          const ps_task* tasks, int32_t n_tasks, int32_t kernel, const void* in,
+                          const float* h_in, void* out, hipStream_t hs);
+
 /* ------------------------------------------------------------------ head --
  * The steps either side of the block stack (a Wan-style reading; the pages
  * evaluate Wan-family backbones -- AREX article on the PhysisServe report,
@@ -279,6 +351,10 @@ ps_status ps_output_head(ps_head* head, ps_time_embed* te, const float* t, int32
                          int32_t tokens, const float* h, float* v, hipStream_t hs);
 
 /* ----------------------------------------------------------------- euler --
+ * Each chunk passes its denoising steps one after another, step s + 1
+ * starting from the latent step s produced (AREX article, "难题"; 163.com
+ * release, "新一代物理 AI 的基础设施", Fig. 1).  The update between steps is
+ * the flow-matching Euler step of the Wan-family backbones the pages name.
  * Flow-matching Euler step after the last block: for task i,
  *   x[i] <- x[i] - dt[i] * v[i],  dt[i] = t_s - t_{s+1} (t_S = 0).
  * x: device fp32 [n_tasks * tokens, hidden]; v: device [n_tasks * tokens,
@@ -286,6 +362,13 @@ ps_status ps_output_head(ps_head* head, ps_time_embed* te, const float* t, int32
 ps_status ps_euler_update(float* x, const void* v, const float* dt, int32_t n_tasks,
                           int32_t tokens, int32_t hidden, ps_dtype v_dtype,
                           hipStream_t hs);
+/* The same step with dt taken from the schedule: task i is at step steps[i]
+ * of timesteps[0 .. n_steps - 1] (host float; t_{n_steps} = 0), so that
+ * dt[i] = timesteps[steps[i]] - timesteps[steps[i] + 1] in fp32.  steps: host
+ * int32 [n_tasks], each in [0, n_steps). */
+ps_status ps_euler_update_steps(float* x, const void* v, const float* timesteps, int32_t n_steps,
+                                const int32_t* steps, int32_t n_tasks, int32_t tokens,
+                                int32_t hidden, ps_dtype v_dtype, hipStream_t hs);
 
 /* Message of the last failure on this host thread ("" if none). */
 const char* ps_last_error(void);

@@ -17,9 +17,9 @@ only by the readings of the pages listed in the design notes; the pages print
 no worked numeric example of the block.
 """
 from .block import (  # noqa: F401
-    attention, block_task, context_kv, gelu_tanh, layer_norm, modulation,
-    qkv_phase, rest_phase, rope3d, rope_segments, silu, sinusoid, time_embedding,
-    token_positions,
+    adaln, attention, block_task, context_kv, cross_q, ffn_hidden, gelu_tanh, layer_norm,
+    modulation, qkv_phase, qkv_proj, residual, rest_phase, rope3d, rope_segments, silu, sinusoid,
+    time_embedding, token_positions,
 )
 from .head import output_head, patch_embed, patchify, time_mlp, unpatchify  # noqa: F401
 from .schedule import RingPool, run_schedule, shifted_timesteps, staggered_ticks  # noqa: F401

@@ -151,6 +151,50 @@ def context_kv(ctx, w, heads):
     return kv[:, :D].reshape(-1, heads, D // heads), kv[:, D:].reshape(-1, heads, D // heads)
 
 
+def adaln(h, shift=None, scale=None):
+    """The block's normalisation step: LN(h)(1 + scale) + shift, or plain LN(h)
+    without modulation (the cross-attention pre-norm).  [L, D] -> [L, D]."""
+    y = layer_norm(h)
+    if scale is None:
+        return y
+    return y * (1.0 + scale) + shift
+
+
+def qkv_proj(y, w, chunk, grid, heads):
+    """Queries, keys and values of the self-attention: y Wqkv + bqkv split into
+    (q | k | v), then RoPE3D on q and k at the chunk's token positions.
+    y [L, D] -> q, k, v [L, H, d]; (k, v) is the chunk's noisy-KV cache entry."""
+    y = np.asarray(y, dtype=F64)
+    L, D = y.shape
+    d = D // heads
+    qkv = _lin(y, w["wqkv"], w["bqkv"])
+    q = qkv[:, :D].reshape(L, heads, d)
+    k = qkv[:, D:2 * D].reshape(L, heads, d)
+    v = qkv[:, 2 * D:].reshape(L, heads, d)
+    pos = token_positions(chunk, grid)
+    return rope3d(q, pos), rope3d(k, pos), v
+
+
+def residual(h, x, wmat, bias, gate=None):
+    """The residual update after a branch: h + gate * (x W + b), or h + (x W + b)
+    without a gate (the cross-attention branch).  [L, D] -> [L, D]."""
+    h = np.asarray(h, dtype=F64)
+    z = _lin(np.asarray(x, dtype=F64), wmat, bias)
+    return h + z if gate is None else h + gate * z
+
+
+def cross_q(y2, w, heads):
+    """Cross-attention queries y2 Wq2 + bq2: [L, D] -> [L, H, d]."""
+    y2 = np.asarray(y2, dtype=F64)
+    L, D = y2.shape
+    return _lin(y2, w["wq2"], w["bq2"]).reshape(L, heads, D // heads)
+
+
+def ffn_hidden(y3, w):
+    """The FFN's hidden activation GELU_tanh(y3 W1 + b1): [L, D] -> [L, F]."""
+    return gelu_tanh(_lin(np.asarray(y3, dtype=F64), w["w1"], w["b1"]))
+
+
 def qkv_phase(h, mod, w, chunk, grid, heads, trace=None):
     """Self-attention inputs of one task: y = LN(h)(1 + scale1) + shift1;
     q, k, v = y Wqkv + b; RoPE3D on q and k at the chunk's token positions.
@@ -160,14 +204,8 @@ def qkv_phase(h, mod, w, chunk, grid, heads, trace=None):
     the intermediates y1 and q ([L, D])."""
     h = np.asarray(h, dtype=F64)
     L, D = h.shape
-    d = D // heads
-    y = layer_norm(h) * (1.0 + mod[1]) + mod[0]
-    qkv = _lin(y, w["wqkv"], w["bqkv"])
-    q = qkv[:, :D].reshape(L, heads, d)
-    k = qkv[:, D:2 * D].reshape(L, heads, d)
-    v = qkv[:, 2 * D:].reshape(L, heads, d)
-    pos = token_positions(chunk, grid)
-    q, k = rope3d(q, pos), rope3d(k, pos)
+    y = adaln(h, mod[0], mod[1])
+    q, k, v = qkv_proj(y, w, chunk, grid, heads)
     if trace is not None:
         trace["y1"], trace["q"] = y, q.reshape(L, D)
     return q, k, v
@@ -191,16 +229,16 @@ def rest_phase(h, q, K, V, mod, w, ctx_k, ctx_v, rows=None, trace=None):
     L, D = h.shape
     heads = q.shape[1]
     a = attention(q, K, V).reshape(L, D)
-    h1 = h + mod[2] * _lin(a, w["wo"], w["bo"])
-    y2 = layer_norm(h1)
-    q2 = _lin(y2, w["wq2"], w["bq2"]).reshape(L, heads, D // heads)
+    h1 = residual(h, a, w["wo"], w["bo"], gate=mod[2])
+    y2 = adaln(h1)
+    q2 = cross_q(y2, w, heads)
     a2 = attention(q2, ctx_k, ctx_v).reshape(L, D)
-    h2 = h1 + _lin(a2, w["wo2"], w["bo2"])
-    y3 = layer_norm(h2) * (1.0 + mod[4]) + mod[3]
-    u = gelu_tanh(_lin(y3, w["w1"], w["b1"]))
+    h2 = residual(h1, a2, w["wo2"], w["bo2"])
+    y3 = adaln(h2, mod[3], mod[4])
+    u = ffn_hidden(y3, w)
     if trace is not None:
         trace.update(attn=a, h1=h1, y2=y2, q2=q2.reshape(L, D), xattn=a2, h2=h2, y3=y3, u=u)
-    return h2 + mod[5] * _lin(u, w["w2"], w["b2"])
+    return residual(h2, u, w["w2"], w["b2"], gate=mod[5])
 
 
 def block_task(h, e, w, chunk, prior_kv, ctx_kv, grid, heads, rows=None, trace=None):

@@ -134,5 +134,31 @@ def test_shifted_timesteps_match_the_oracle(S, shift):
     from autoregressive_denoising_dit_amd.schedule import shifted_timesteps
     got, ref = shifted_timesteps(S, shift), oracle.shifted_timesteps(S, shift)
     assert len(got) == S
+    # the library returns fp32 timesteps (a task's timestep is fp32): the
+    # oracle's value rounded to fp32, give or take one ulp at a rounding tie
     for a, b in zip(got, ref):
-        assert a == pytest.approx(b, rel=1e-15, abs=0)
+        assert a == pytest.approx(b, rel=2.0 ** -23, abs=0)
+
+
+def test_new_entry_points_reject_bad_arguments():
+    """Host-side validation of the calls that need no GPU to reject."""
+    lib = _lib.load()
+    out = (C.c_float * 5)()
+    assert lib.ps_timesteps(0, C.c_float(1.0), out) == _lib.PS_ERR_INVALID_ARG
+    assert lib.ps_timesteps(4, C.c_float(0.0), out) == _lib.PS_ERR_INVALID_ARG
+    assert lib.ps_timesteps(4, C.c_float(float("nan")), out) == _lib.PS_ERR_INVALID_ARG
+    assert lib.ps_timesteps(4, C.c_float(1.0), None) == _lib.PS_ERR_INVALID_ARG
+    assert lib.ps_timesteps(4, C.c_float(1.0), out) == _lib.PS_OK
+    assert list(out) == [1.0, 0.75, 0.5, 0.25, 0.0]
+    ts = (C.c_float * 4)(1.0, 0.75, 0.5, 0.25)
+    steps = (C.c_int32 * 1)(4)                                   # step out of range
+    assert lib.ps_euler_update_steps(C.c_void_p(16), C.c_void_p(16), ts, 4, steps, 1, 64, 128, 0,
+                                     None) == _lib.PS_ERR_INVALID_ARG
+    assert b"out of range" in lib.ps_last_error()
+    assert lib.ps_euler_update_steps(C.c_void_p(16), C.c_void_p(16), None, 4, steps, 1, 64, 128, 0,
+                                     None) == _lib.PS_ERR_INVALID_ARG
+    assert lib.ps_stage_kernel(None, None, None, None, 1, 99, None, None, None, None) == _lib.PS_ERR_INVALID_ARG
+    assert b"unknown kernel" in lib.ps_last_error()
+    assert lib.ps_stage_kernel(None, None, None, None, 1, 3, None, None, None, None) == _lib.PS_ERR_INVALID_ARG
+    assert lib.ps_context_load(None, 0, 0, None, None, 8, None) == _lib.PS_ERR_INVALID_ARG
+    assert lib.ps_kv_pool_release_stream(None, None) == _lib.PS_ERR_INVALID_ARG
