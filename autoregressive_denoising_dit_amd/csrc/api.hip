@@ -781,7 +781,8 @@ ps_status ps::prepare_batch(const ps_kv_pool* p, const ps_block* b, const ps_tim
   return PS_OK;
 }
 
-WsSizes ps::ws_sizes(const ps_kv_pool* p, const ps_block_desc& bd, int n) {
+WsSizes ps::ws_sizes(const ps_kv_pool* p, const ps_block* b, int n) {
+  const ps_block_desc& bd = b->d;
   const size_t M = (size_t)n * p->L(), es = elt_size(bd.dtype);
   const size_t D = bd.hidden, F = bd.ffn;
   return WsSizes{{sizeof(float) * n * 6 * D, sizeof(float2) * n * p->desc.frames * (size_t)(p->seg_f / 2) + 16,
@@ -991,7 +992,7 @@ static ps_status stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te
   ps_status st = prepare_batch(p, b, te, tasks, n, h_in, h_out, "ps_stage_batch", &bt);
   if (st) return st;
   WsPtrs w;
-  if ((st = ws_from_pool(p, ws_sizes(p, b->d, n), hs, &w))) return st;
+  if ((st = ws_from_pool(p, ws_sizes(p, b, n), hs, &w))) return st;
   if ((st = begin_batch(p, b, te, bt, w, hs))) return st;
   if ((st = run_stage_dt(p, b, w, n, stage_io(h_in, h_out), probe, -1, hs))) return st;
   commit_writes(p, bt, tasks);
@@ -1025,7 +1026,7 @@ extern "C" ps_status ps_stage_kernel(ps_kv_pool* p, const ps_block* b, ps_time_e
   ps_status st = prepare_batch(p, b, te, tasks, n, in, out, fn, &bt);
   if (st) return st;
   WsPtrs w;
-  if ((st = ws_from_pool(p, ws_sizes(p, b->d, n), hs, &w))) return st;
+  if ((st = ws_from_pool(p, ws_sizes(p, b, n), hs, &w))) return st;
   if ((st = begin_batch(p, b, te, bt, w, hs))) return st;
   const int L = p->L(), D = b->d.hidden, F = b->d.ffn;
   const size_t M = (size_t)n * L, es = elt_size(b->d.dtype);

@@ -34,7 +34,7 @@ struct WsSizes {
 // Every check of a stage call; nothing is enqueued or changed.
 ps_status prepare_batch(const ps_kv_pool* p, const ps_block* b, const ps_time_embed* te, const ps_task* tasks,
                         int32_t n, const void* h_in, const void* h_out, const char* fn, Batch* out);
-WsSizes ws_sizes(const ps_kv_pool* p, const ps_block_desc& bd, int n);
+WsSizes ws_sizes(const ps_kv_pool* p, const ps_block* b, int n);
 // Bytes of one contiguous region holding all buffers (each 256-byte aligned).
 size_t ws_total(const WsSizes& z);
 // The buffers laid out from base (ws_total(z) bytes, 256-byte aligned).

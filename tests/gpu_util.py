@@ -87,9 +87,10 @@ class StageCase:
         self.h_in = inputs.hidden_rows(cfg, len(tasks), seed)
 
     # ---------------------------------------------------------------- GPU
-    def run_gpu(self, h_out_same=False, probe=False):
+    def setup_gpu(self):
+        """Pool (contexts set from the seeded tokens, window slots pre-filled),
+        block and timestep embedding on the GPU; returns the batch's tasks."""
         cfg = self.cfg
-        say("stage", cfg.name, "tasks", self.tasks)
         self.pool = make_pool(cfg, n_streams=self.n_streams, n_blocks=self.block_index + 1, n_slots=self.R)
         self.block = make_block(cfg, self.w, self.block_index)
         self.te = make_te(cfg, self.tw)
@@ -97,9 +98,15 @@ class StageCase:
             self.pool.context_set(self.block, sg, to_dev(ctx, self.td))
         for (sg, s, j), (k, v) in self.prefill.items():
             self.pool.load(sg, self.block_index, s, j % self.R, j, to_dev(k, self.td), to_dev(v, self.td))
-        ps_tasks = [runtime.make_task(sg, c, s, cfg.timesteps[s], c % self.R,
-                                      [j % self.R for j in range(c - nr, c)])
-                    for (sg, c, s, nr) in self.tasks]
+        self.ps_tasks = [runtime.make_task(sg, c, s, cfg.timesteps[s], c % self.R,
+                                           [j % self.R for j in range(c - nr, c)])
+                         for (sg, c, s, nr) in self.tasks]
+        return self.ps_tasks
+
+    def run_gpu(self, h_out_same=False, probe=False):
+        cfg = self.cfg
+        say("stage", cfg.name, "tasks", self.tasks)
+        ps_tasks = self.setup_gpu()
         h_in = to_dev(self.h_in, torch.float32)
         h_out = h_in if h_out_same else torch.empty_like(h_in)
         if probe:
@@ -121,14 +128,10 @@ class StageCase:
         return self
 
     # ------------------------------------------------------------- oracle
-    def run_oracle(self, task_ids=None, rows=None, attn_rounding=False):
+    def run_oracle(self, task_ids=None, rows=None):
         """Oracle h_out rows (all or a sample), cache entries of the tasks and
         each task's intermediates (self.ref_trace[i]: y1 and q over all rows,
-        the rest over ``rows``).  With ``attn_rounding`` (bf16 workloads) the
-        trace also holds "attn_rb" and "xattn_rb": both attentions evaluated by
-        the oracle on its own queries, keys and values rounded to bf16, the
-        precision they are stored in -- a measure of how far that storage
-        alone moves the attention outputs."""
+        the rest over ``rows``)."""
         cfg, L = self.cfg, self.cfg.tokens
         ids = range(len(self.tasks)) if task_ids is None else task_ids
         E = {s: oracle.time_embedding(t, self.tw) for s, t in enumerate(cfg.timesteps)}
@@ -163,18 +166,6 @@ class StageCase:
                 ctx_kv[sg] = oracle.context_kv(self.ctx[sg], self.w, cfg.heads)
             tr = dict(own_trace[(sg, s, c)])
             out[i] = oracle.rest_phase(h, q, K, V, mod, self.w, *ctx_kv[sg], rows=rows, trace=tr)
-            if attn_rounding and cfg.dtype == "bf16":
-                def rb(a):
-                    return inputs.round_bf16(np.asarray(a, np.float32)).astype(np.float64)
-                qr = q if rows is None else q[rows]
-                n_r = qr.shape[0]
-                tr["attn_rb"] = oracle.attention(rb(qr), rb(K), rb(V)).reshape(n_r, cfg.hidden)
-                tr["xattn_rb"] = oracle.attention(rb(tr["q2"]).reshape(qr.shape), rb(ctx_kv[sg][0]),
-                                                  rb(ctx_kv[sg][1])).reshape(n_r, cfg.hidden)
-                # the two attention branches' deltas of the residual stream with those outputs
-                f64 = lambda a: np.asarray(a, np.float64)
-                tr["h1 - h_rb"] = mod[2] * (tr["attn_rb"] @ f64(self.w["wo"]) + f64(self.w["bo"]))
-                tr["h2 - h1_rb"] = tr["xattn_rb"] @ f64(self.w["wo2"]) + f64(self.w["bo2"])
             self.ref_trace[i] = tr
         self.ref_h_out = out
         self.ref_kv = {(sg, c, s): own[(sg, s, c)][1:] for (sg, c, s, _) in self.tasks if (sg, s, c) in own}

@@ -20,7 +20,10 @@ from tests.gpu_util import (StageCase, host, make_block, make_pool, make_te, rel
 pytestmark = pytest.mark.gpu
 
 
-def _check_case(case, task_ids=None, rows=None):
+def _check_case(case, task_ids=None, rows=None, delta=True):
+    """The stage output h_out and the cache entries written, at the bound
+    (north_star's "output"); with ``delta`` also the branch delta h_out - h_in,
+    which is small next to the residual stream."""
     cfg, L = case.cfg, case.cfg.tokens
     t = tol(cfg)
     ids = list(range(len(case.tasks))) if task_ids is None else task_ids
@@ -34,7 +37,7 @@ def _check_case(case, task_ids=None, rows=None):
         e_delta = rel_err(got - h, ref - h)
         say(f"task {i} {case.tasks[i]}: h_out err {e_out:.2e}, branch delta err {e_delta:.2e}")
         assert e_out <= t, (i, e_out)
-        assert e_delta <= t, (i, e_delta)
+        assert e_delta <= t or not delta, (i, e_delta)
         key = (case.tasks[i][0], case.tasks[i][1], case.tasks[i][2])
         if key in case.ref_kv:
             k_ref, v_ref = case.ref_kv[key]
@@ -54,23 +57,17 @@ def _probe_err(got, ref, allow):
 
 
 def _check_probe(case, task_ids=None, rows=None):
-    """Each kernel's output (ps_stage_batch_probe) against the oracle's matching
-    intermediate, task by task.  A stored member carries its own rounding, at
+    """Each kernel's output in the chain of one stage call
+    (ps_stage_batch_probe) against the oracle's matching intermediate, task by
+    task, at the plain bound.  A stored member carries its own rounding, at
     most the unit roundoff of its storage type times the value (2^-8 in bf16,
-    2^-24 in fp32); that allowance is taken off each element's error before the
-    bound max|err| / RMS(ref) <= tol is applied.  The same holds for the branch
-    deltas h1 - h and h2 - h1, whose operands are stored fp32 values that are
-    large next to the delta.  The queries are stored times log2(e)/sqrt(d),
-    which is divided out.
-
-    The attention outputs also inherit the bf16 storage of their queries,
-    keys and values, amplified by the softmax: with the logits of the 14B
-    shape (max near 9) that alone moves single outputs by several percent of
-    the RMS.  Their bound, and that of the branch deltas computed from them,
-    is therefore tol + 2 e_rb, where e_rb is that movement as the oracle
-    measures it on its own values (the "*_rb" trace members); twice, because
-    the kernel's queries and keys carry two roundings of that size, their own
-    and that of the bf16 activations they are computed from."""
+    2^-24 in fp32); that is taken off each element's error before the bound
+    max|err| / RMS(ref) <= tol applies.  The same holds for the branch deltas
+    h1 - h and h2 - h1, whose operands are stored fp32 values that are large
+    next to the delta.  The queries are stored times log2(e)/sqrt(d), which is
+    divided out.  In the chain every kernel also inherits the rounding of its
+    inputs; each kernel on its own, on identical inputs, is scored in
+    test_gpu_kernels.py."""
     cfg, L = case.cfg, case.cfg.tokens
     t = tol(cfg)
     u32 = UNIT_ROUNDOFF["fp32"]
@@ -88,11 +85,8 @@ def _check_probe(case, task_ids=None, rows=None):
                 got = got / qscale
             u = u32 if name in _lib.PROBE_FP32 else UNIT_ROUNDOFF[cfg.dtype]
             err = _probe_err(got, ref, u * np.abs(ref))
-            bound = t
-            if name + "_rb" in tr:
-                bound = t + 2.0 * rel_err(tr[name + "_rb"], ref)
-            say(f"task {i} probe {name}: err {err:.2e} (plain {rel_err(got, ref):.2e}), bound {bound:.2e}")
-            assert err <= bound, (i, name, err, bound)
+            say(f"task {i} probe {name}: err {err:.2e} (plain {rel_err(got, ref):.2e})")
+            assert err <= t, (i, name, err)
             got_h[name] = got
         # the gated / plain branch deltas, which are small next to the residual stream
         h = case.h_in[i * L:(i + 1) * L] if rows is None else case.h_in[i * L:(i + 1) * L][rows]
@@ -100,11 +94,8 @@ def _check_probe(case, task_ids=None, rows=None):
                 ("h1 - h", got_h["h1"], h, tr["h1"], h, u32 * np.abs(tr["h1"])),
                 ("h2 - h1", got_h["h2"], got_h["h1"], tr["h2"], tr["h1"], u32 * (np.abs(tr["h2"]) + np.abs(tr["h1"])))):
             e = _probe_err(a - b, ra - rb, allow)
-            bound = t
-            if name + "_rb" in tr:
-                bound = t + 2.0 * rel_err(tr[name + "_rb"], ra - rb)
-            say(f"task {i} probe {name}: err {e:.2e} (plain {rel_err(a - b, ra - rb):.2e}), bound {bound:.2e}")
-            assert e <= bound, (i, name, e, bound)
+            say(f"task {i} probe {name}: err {e:.2e} (plain {rel_err(a - b, ra - rb):.2e})")
+            assert e <= t, (i, name, e)
 
 
 # ----------------------------------------------------------------- pieces
@@ -131,8 +122,15 @@ def test_context_keys_values(cfg):
         pool.context_set(blk, sg, to_dev(ctx, td))
         k, v = pool.context_fetch(sg, 0, cfg.n_ctx)
         rk, rv = oracle.context_kv(ctx, w, cfg.heads)
-        assert rel_err(host(k), rk) <= tol(cfg)
-        assert rel_err(host(v), rv) <= tol(cfg)
+        # one GEMM, then the rounding of its output to the compute dtype (at
+        # most 2^-8 / 2^-24 of each value, taken off as in the probe checks);
+        # what remains is fp32 accumulation error, far inside the bound, so a
+        # third of it is required
+        u = UNIT_ROUNDOFF[cfg.dtype]
+        ek = _probe_err(host(k), rk, u * np.abs(rk))
+        ev = _probe_err(host(v), rv, u * np.abs(rv))
+        say(f"context k err {ek:.2e}, v err {ev:.2e} (plain {rel_err(host(k), rk):.2e}, {rel_err(host(v), rv):.2e})")
+        assert ek <= tol(cfg) / 3 and ev <= tol(cfg) / 3
 
 
 @pytest.mark.parametrize("vdt", [torch.float32, torch.bfloat16])
@@ -166,7 +164,7 @@ def test_stage_fp32_tiny_mixed_batch():
     cfg = C1
     tasks = [(0, 0, 0, 0), (0, 3, 1, 2), (0, 2, 0, 2), (0, 1, 1, 1)]
     case = StageCase(cfg, tasks, n_slots=8).run_gpu()
-    case.run_oracle(attn_rounding=True)
+    case.run_oracle()
     _check_case(case)
 
 
@@ -245,40 +243,8 @@ def test_stage_probe_kernels_fp32_tiny():
 def test_stage_probe_kernels_c2_full():
     """Each kernel's output at the 1.3B shape, batch 1, full window, every row."""
     case = StageCase(C2, [(0, 7, 2, 3)]).run_gpu(probe=True)
-    case.run_oracle(attn_rounding=True)
+    case.run_oracle()
     _check_probe(case)
-
-
-def test_stage_probe_kernels_c3_c4_sampled():
-    """Each kernel's output in a time-shared batch of 8 at the 1.3B shape (two
-    chunks per step at all four steps, one reading the other's same-batch
-    write) and in a 5B-shaped batch (1760-token chunks: ragged last query
-    and key tiles); sampled rows."""
-    tasks = []
-    for s in range(4):
-        for j in range(2):
-            c = 2 * (5 - s) + j
-            tasks.append((0, c, s, min(C3.window, c)))
-    case = StageCase(C3, tasks, n_slots=C3.window + 2).run_gpu(probe=True)
-    rows = np.array([0, 1, 100, 777, 1200, 1559])
-    case.run_oracle(task_ids=[1, 6], rows=rows, attn_rounding=True)
-    _check_probe(case, task_ids=[1, 6], rows=rows)
-    del case
-    case = StageCase(C4, [(0, 9, 3, 3), (0, 12, 0, 3)]).run_gpu(probe=True)
-    rows = np.array([0, 43, 44, 901, 1727, 1759])
-    case.run_oracle(task_ids=[0, 1], rows=rows, attn_rounding=True)
-    _check_probe(case, task_ids=[0, 1], rows=rows)
-
-
-def test_stage_probe_kernels_c5_sampled():
-    """Each kernel's output in the 16-task batch of the 14B shape that the
-    benchmark times (sampled rows of two tasks)."""
-    cfg = C5
-    tasks = [(i, 10 + i // 4, (i * 3) % 4, 3) for i in range(16)]
-    case = StageCase(cfg, tasks, share_prefill=True).run_gpu(probe=True)
-    rows = np.array([0, 31, 32, 517, 1536, 1559])
-    case.run_oracle(task_ids=[2, 15], rows=rows, attn_rounding=True)
-    _check_probe(case, task_ids=[2, 15], rows=rows)
 
 
 def test_stage_c2_single_task_full():
@@ -302,9 +268,9 @@ def test_stage_batch_invariance_bitwise_c2_shape():
         assert np.array_equal(x, y)
 
 
-def test_stage_c3_mixed_steps_sampled():
+def test_stage_c3_mixed_steps_full():
     """1.3B shape, a time-shared batch of 8 tasks: 2 chunks per step at all 4
-    steps (k = 2, ring W + 2); sampled rows of two tasks checked."""
+    steps (k = 2, ring W + 2); every row of all 8 tasks."""
     cfg = C3
     tasks = []
     for s in range(4):
@@ -312,9 +278,8 @@ def test_stage_c3_mixed_steps_sampled():
             c = 2 * (5 - s) + j
             tasks.append((0, c, s, min(cfg.window, c)))
     case = StageCase(cfg, tasks, n_slots=cfg.window + 2).run_gpu()
-    rows = np.array([0, 1, 100, 777, 1200, 1559])
-    case.run_oracle(task_ids=[1, 6], rows=rows)
-    _check_case(case, task_ids=[1, 6], rows=rows)
+    case.run_oracle()
+    _check_case(case)
 
 
 def test_stage_bf16_largest_batch_c3_shape():
@@ -332,24 +297,54 @@ def test_stage_bf16_largest_batch_c3_shape():
     _check_case(case, task_ids=ids, rows=rows)
 
 
-def test_stage_c4_sampled():
+def test_stage_c4_full():
+    """5B shape (1760-token chunks), two tasks at different steps; every row."""
     cfg = C4
     tasks = [(0, 9, 3, 3), (0, 12, 0, 3)]
     case = StageCase(cfg, tasks).run_gpu()
-    rows = np.array([0, 43, 44, 901, 1759])
-    case.run_oracle(task_ids=[0, 1], rows=rows)
-    _check_case(case, task_ids=[0, 1], rows=rows)
+    case.run_oracle()
+    _check_case(case)
 
 
-def test_stage_c5_sixteen_streams_sampled():
+def test_stage_c5_sixteen_streams_full_rows():
     """14B-shaped stage, the batch of 16 tasks from 16 streams at mixed steps
-    that the benchmark times; sampled rows of two tasks checked."""
+    that the benchmark times; every row of one task per denoising step.
+
+    The stage output and the cache entries are held to the bound.  The branch
+    delta h_out - h_in is not: at this width the bf16 storage of the block's
+    intermediates alone -- the oracle's float64 chain with only those values
+    rounded -- moves the delta of task 0 by 3.4e-2 of its RMS
+    (test_oracle_block.py::test_bf16_storage_alone_moves_the_14b_branch_delta),
+    so no bf16 implementation meets 3e-2 there.  The branches are held to the
+    bound kernel by kernel on identical inputs (test_gpu_kernels.py)."""
     cfg = C5
     tasks = [(i, 10 + i // 4, (i * 3) % 4, 3) for i in range(16)]
+    assert sorted(tasks[i][2] for i in range(4)) == [0, 1, 2, 3]
     case = StageCase(cfg, tasks, share_prefill=True).run_gpu()
-    rows = np.array([0, 517, 1559])
-    case.run_oracle(task_ids=[0, 13], rows=rows)
-    _check_case(case, task_ids=[0, 13], rows=rows)
+    case.run_oracle(task_ids=[0, 1, 2, 3])
+    _check_case(case, task_ids=[0, 1, 2, 3], delta=False)
+
+
+def test_stage_two_frame_chunks():
+    """Chunks of two latent frames (grid 2 x 24 x 32): the frame index of a
+    token and the per-frame rows of the RoPE frame table; every row, with the
+    probe of each kernel."""
+    cfg = with_(C2, hidden=512, heads=4, head_dim=128, ffn=1024, grid=(2, 24, 32), n_ctx=64)
+    case = StageCase(cfg, [(0, 5, 1, 3), (0, 6, 1, 3), (1, 2, 3, 2)], n_slots=5).run_gpu(probe=True)
+    case.run_oracle()
+    _check_case(case)
+    _check_probe(case)
+
+
+def test_stage_rope_tables_beyond_lds():
+    """A 60 x 88 token grid: the row and column RoPE tables (3152 pairs with the
+    frame rows) exceed the QKV epilogue's LDS budget, so the epilogue reads
+    them from memory; every row."""
+    cfg = with_(C2, hidden=512, heads=4, head_dim=128, ffn=1024, grid=(1, 60, 88), n_ctx=64)
+    case = StageCase(cfg, [(0, 4, 2, 3), (1, 1, 0, 1)]).run_gpu(probe=True)
+    case.run_oracle()
+    _check_case(case)
+    _check_probe(case)
 
 
 # ------------------------------------------------------------- schedules
@@ -361,7 +356,7 @@ def _schedule_inputs(cfg, n_chunks, n_streams, seed=0):
     return blocks, tw, ctxs, lat
 
 
-def _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, n_streams, k):
+def _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, n_streams, k, keep_pool=False):
     from autoregressive_denoising_dit_amd.schedule import StaggeredRunner
     td = runtime.TORCH_DTYPE[runtime.ps_dtype(cfg.dtype)]
     pool = make_pool(cfg, n_streams=n_streams, n_blocks=cfg.n_blocks, n_slots=cfg.window + k)
@@ -375,7 +370,7 @@ def _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, n_streams, k):
     run = StaggeredRunner(pool, blks, te, cfg.timesteps, cfg.window, k, n_streams)
     run.run(x, n_chunks)
     torch.cuda.synchronize()
-    return host(x)
+    return (host(x), pool) if keep_pool else host(x)
 
 
 @pytest.mark.parametrize("k,n_streams", [(1, 1), (2, 1), (1, 2)])
@@ -407,6 +402,38 @@ def test_schedule_batch_invariance_bitwise_c3_shape():
     b = _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, 1, 1)
     assert np.array_equal(a, b)
     assert np.all(np.isfinite(a))
+
+
+def test_schedule_bf16_c3_shape_matches_oracle():
+    """The 1.3B shape in bf16 end to end at reduced depth: 2 blocks x 4 steps,
+    7 chunks, k = 2 (block batches of up to 8 tasks at mixed steps, chunk c + 1
+    reading chunk c's same-batch write), staggered on the GPU against the
+    oracle's sequential run.  Scored at the bf16 bound: every chunk's x^S and
+    x^0 - x^S, and the noisy-KV entries the run leaves in the pool (the last
+    W + k chunks of every (block, step)), which carry the hand-off of noisy KV
+    between chunks across blocks and steps."""
+    cfg = with_(C3, n_blocks=2)
+    n_chunks, k = 7, 2
+    blocks, tw, ctxs, lat = _schedule_inputs(cfg, n_chunks, 1)
+    say("schedule bf16 1.3B shape, 2 blocks x 4 steps, 7 chunks, k = 2")
+    gx, pool = _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, 1, k, keep_pool=True)
+    ox, opool = oracle.run_schedule(cfg, blocks, tw, lambda sg, c: lat[(sg, c)], ctxs, n_chunks,
+                                    order="sequential", k=k)
+    t = tol(cfg)
+    for c in range(n_chunks):
+        x0 = lat[(0, c)].astype(np.float64)
+        e, ed = rel_err(gx[c, 0], ox[(0, c)]), rel_err(x0 - gx[c, 0], x0 - ox[(0, c)])
+        say(f"chunk {c}: x^S err {e:.2e}, x^0 - x^S err {ed:.2e}")
+        assert e <= t and ed <= t
+    R = cfg.window + k
+    for b in range(cfg.n_blocks):
+        for s in range(cfg.n_steps):
+            for slot in range(R):
+                chunk, kr, vr = opool.slots[(0, b, s, slot)]
+                kg, vg = pool.fetch(0, b, s, slot)
+                ek, ev = rel_err(host(kg), kr), rel_err(host(vg), vr)
+                say(f"block {b} step {s} slot {slot} (chunk {chunk}): k err {ek:.2e}, v err {ev:.2e}")
+                assert ek <= t and ev <= t
 
 
 # ------------------------------------------------- patch embedding / head

@@ -322,3 +322,52 @@ def test_block_identity_with_zero_gates():
     ck = oracle.context_kv(r.standard_normal((cfg.n_ctx, D)), w, H)
     out, _ = oracle.block_task(h, e, w, 0, [], ck, cfg.grid, H)
     np.testing.assert_array_equal(out, h)
+
+
+@pytest.mark.slow
+def test_bf16_storage_alone_moves_the_14b_branch_delta():
+    """A measurement behind the bf16 bound at the 14B shape: the oracle's
+    float64 block with only the values a bf16 path stores rounded to bf16
+    (LN outputs, queries, keys, values, context keys/values, attention outputs,
+    FFN hidden; the residual stream stays exact) against the unrounded block,
+    for task 0 of the 16-stream batch (stream 0, chunk 10, step 0, full
+    window).  The stage output moves by less than 3e-2 of its RMS, but the
+    branch delta h_out - h_in by more: at this width the softmax is sharp
+    enough that bf16 queries and keys alone move the self-attention branch by
+    about 10% of its RMS.  So 3e-2 on the branch delta is beyond any bf16
+    implementation here, and the branches are held to the bound kernel by
+    kernel on identical inputs instead."""
+    from synthetic import C5
+    cfg = C5
+    w = inputs.block_weights(cfg, 0, 0)
+    tw = inputs.time_weights(cfg, 0)
+    L, H, D = cfg.tokens, cfg.heads, cfg.hidden
+    h = inputs.hidden_rows(cfg, 16, 0)[:L]
+    c, s = 10, 0
+    mod = oracle.modulation(oracle.time_embedding(cfg.timesteps[s], tw), w["tmod"])
+    prior = [inputs.cache_entry(cfg, 0, 0, s, j, 0) for j in range(c - 3, c)]
+    ck, cv = oracle.context_kv(inputs.context(cfg, 0, 0), w, H)
+
+    def chain(r):
+        y1 = r(oracle.adaln(h, mod[0], mod[1]))
+        q, k, v = (r(x) for x in oracle.qkv_proj(y1, w, c, cfg.grid, H))
+        K = np.concatenate([p[0] for p in prior] + [k])
+        V = np.concatenate([p[1] for p in prior] + [v])
+        h1 = oracle.residual(h, r(oracle.attention(q, K, V).reshape(L, D)), w["wo"], w["bo"], gate=mod[2])
+        q2 = r(oracle.cross_q(r(oracle.adaln(h1)), w, H))
+        h2 = oracle.residual(h1, r(oracle.attention(q2, r(ck), r(cv)).reshape(L, D)), w["wo2"], w["bo2"])
+        u = r(oracle.ffn_hidden(r(oracle.adaln(h2, mod[3], mod[4])), w))
+        return h1, oracle.residual(h2, u, w["w2"], w["b2"], gate=mod[5])
+
+    def rb(a):
+        return inputs.round_bf16(np.asarray(a, np.float32)).astype(np.float64)
+
+    ex1, ex = chain(lambda a: np.asarray(a, np.float64))
+    bf1, bf = chain(rb)
+
+    def rel(g, r_):
+        return np.abs(g - r_).max() / np.sqrt(np.mean(r_ ** 2))
+
+    assert rel(bf, ex) < 3e-2                 # the stage output: inside the bound
+    assert rel(bf - h, ex - h) > 3e-2         # its branch delta: beyond it (3.4e-2)
+    assert rel(bf1 - h, ex1 - h) > 5e-2       # the self-attention branch alone (about 0.10)
