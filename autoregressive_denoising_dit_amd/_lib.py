@@ -28,6 +28,7 @@ KERNELS = ("ln1", "qkv", "attn_self", "o_proj", "ln2", "xq_proj", "attn_cross", 
 PS_MAX_WINDOW = 8
 PS_MAX_TASKS = 32
 PS_FREQ_DIM = 256
+PS_STATIC_SCRATCH_BYTES = 128 << 20
 
 EXPORTS = (
     "ps_kv_pool_create", "ps_kv_pool_destroy", "ps_kv_pool_load", "ps_kv_pool_fetch",
@@ -37,7 +38,7 @@ EXPORTS = (
     "ps_trace_entry", "ps_head_create", "ps_head_destroy", "ps_patch_embed", "ps_output_head",
     "ps_sched_create", "ps_sched_destroy", "ps_sched_split", "ps_sched_admit", "ps_sched_release",
     "ps_sched_gpu", "ps_kv_pool_release_stream", "ps_context_load", "ps_stage_kernel", "ps_timesteps",
-    "ps_euler_update_steps",
+    "ps_euler_update_steps", "ps_stage_batch_static",
 )
 
 
@@ -133,6 +134,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ps_stage_kernel": [vp, vp, vp, C.POINTER(Task), i32, i32, vp, vp, vp, vp],
         "ps_timesteps": [i32, f32, C.POINTER(C.c_float)],
         "ps_euler_update_steps": [vp, vp, C.POINTER(C.c_float), i32, C.POINTER(i32), i32, i32, i32, i32, vp],
+        "ps_stage_batch_static": [vp, vp, vp, C.POINTER(Task), i32, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libps.so")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "gemm.hip", "attention.hip", "elementwise.hip", "sched.cpp"]
+SOURCES = ["api.hip", "gemm.hip", "attention.hip", "elementwise.hip", "static_ws.hip", "sched.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",

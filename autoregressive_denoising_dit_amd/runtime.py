@@ -288,6 +288,18 @@ def stage_batch(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], h_in
                                   _stream_ptr(cuda_stream)))
 
 
+def stage_batch_static(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], h_in: torch.Tensor,
+                       h_out: torch.Tensor, cuda_stream=None) -> None:
+    """stage_batch without device allocation (ps_stage_batch_static): the
+    workspace is the library's fixed per-device array."""
+    n = len(tasks)
+    _need(h_in, torch.float32, (n * pool.tokens, pool.hidden), "h_in")
+    _need(h_out, torch.float32, (n * pool.tokens, pool.hidden), "h_out")
+    arr = (Task * max(n, 1))(*tasks)
+    check(pool.lib.ps_stage_batch_static(pool.handle, block.handle, te.handle, arr, n, _ptr(h_in), _ptr(h_out),
+                                         _stream_ptr(cuda_stream)))
+
+
 def stage_batch_probe(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], h_in: torch.Tensor,
                       h_out: torch.Tensor, probe: Dict[str, torch.Tensor], cuda_stream=None) -> None:
     """stage_batch that also copies the intermediates named in `probe`

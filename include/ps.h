@@ -234,6 +234,21 @@ ps_status ps_stage_batch(ps_kv_pool* pool, const ps_block* block, ps_time_embed*
                          const ps_task* tasks, int32_t n_tasks, const float* h_in,
                          float* h_out, hipStream_t hs);
 
+/* ps_stage_batch for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as ps_stage_batch; it neither allocates nor
+ * frees device memory.  Its workspace is one fixed array of
+ * PS_STATIC_SCRATCH_BYTES per device, held from the library's first use on
+ * that device until the process ends: a batch whose workspace needs more
+ * (about 43 MB per task at the 1.3B shape, 92 MB at the 14B shape) is
+ * rejected with PS_ERR_INVALID_ARG before anything is enqueued.  Every call on
+ * a device shares that device's array, so two calls that overlap on one
+ * device (different streams, no ordering between them) race: order them. */
+#define PS_STATIC_SCRATCH_BYTES (128u << 20)
+ps_status ps_stage_batch_static(ps_kv_pool* pool, const ps_block* block, ps_time_embed* te,
+                                const ps_task* tasks, int32_t n_tasks, const float* h_in,
+                                float* h_out, hipStream_t hs);
+
 /* Intermediate activations of one stage batch, for checking each kernel of
  * the path on its own.  Every member is a caller-owned device pointer or
  * NULL (not captured); row i*L + r belongs to task i, rows dense.  Members in

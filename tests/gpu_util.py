@@ -103,7 +103,7 @@ class StageCase:
                          for (sg, c, s, nr) in self.tasks]
         return self.ps_tasks
 
-    def run_gpu(self, h_out_same=False, probe=False):
+    def run_gpu(self, h_out_same=False, probe=False, static=False):
         cfg = self.cfg
         say("stage", cfg.name, "tasks", self.tasks)
         ps_tasks = self.setup_gpu()
@@ -116,6 +116,8 @@ class StageCase:
                                  dtype=torch.float32 if name in _lib.PROBE_FP32 else self.td)
                 for name in _lib.PROBE_FIELDS}
             runtime.stage_batch_probe(self.pool, self.block, self.te, ps_tasks, h_in, h_out, self.gpu_probe)
+        elif static:
+            runtime.stage_batch_static(self.pool, self.block, self.te, ps_tasks, h_in, h_out)
         else:
             runtime.stage_batch(self.pool, self.block, self.te, ps_tasks, h_in, h_out)
         torch.cuda.synchronize()
