@@ -38,7 +38,7 @@ EXPORTS = (
     "ps_trace_entry", "ps_head_create", "ps_head_destroy", "ps_patch_embed", "ps_output_head",
     "ps_sched_create", "ps_sched_destroy", "ps_sched_split", "ps_sched_admit", "ps_sched_release",
     "ps_sched_gpu", "ps_kv_pool_release_stream", "ps_context_load", "ps_stage_kernel", "ps_timesteps",
-    "ps_euler_update_steps", "ps_stage_batch_static",
+    "ps_euler_update_steps", "ps_stage_batch_static", "ps_stage_batch_rows",
 )
 
 
@@ -135,6 +135,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "ps_timesteps": [i32, f32, C.POINTER(C.c_float)],
         "ps_euler_update_steps": [vp, vp, C.POINTER(C.c_float), i32, C.POINTER(i32), i32, i32, i32, i32, vp],
         "ps_stage_batch_static": [vp, vp, vp, C.POINTER(Task), i32, vp, vp, vp],
+        "ps_stage_batch_rows": [vp, vp, vp, C.POINTER(Task), i32, C.POINTER(vp), C.POINTER(vp), vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -206,9 +206,9 @@ struct ps_kv_pool {
   // concurrently (the caller keeps their KV slots apart).
   struct Workspace {
     hipStream_t stream = nullptr;
-    DevBuf mod, rope, y, q, a, u, tasks;
+    DevBuf mod, rope, y, q, a, u, tasks, h;
     void release() {
-      for (DevBuf* b : {&mod, &rope, &y, &q, &a, &u, &tasks}) b->release();
+      for (DevBuf* b : {&mod, &rope, &y, &q, &a, &u, &tasks, &h}) b->release();
     }
   };
   std::vector<Workspace*> ws;
@@ -1002,6 +1002,37 @@ static ps_status stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te
 extern "C" ps_status ps_stage_batch(ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const ps_task* tasks,
                                     int32_t n, const float* h_in, float* h_out, hipStream_t hs) {
   return stage_batch(p, b, te, tasks, n, h_in, h_out, nullptr, hs);
+}
+
+// The residual stream of a batch whose tasks' rows are not one contiguous
+// slice: gathered into the stream's workspace, run in place, scattered back.
+extern "C" ps_status ps_stage_batch_rows(ps_kv_pool* p, const ps_block* b, ps_time_embed* te, const ps_task* tasks,
+                                         int32_t n, const float* const* h_in, float* const* h_out, hipStream_t hs) {
+  const char* fn = "ps_stage_batch_rows";
+  if (!h_in || !h_out) return fail(PS_ERR_INVALID_ARG, "%s: null argument", fn);
+  if (n < 1 || n > PS_MAX_TASKS) return fail(PS_ERR_INVALID_ARG, "%s: n_tasks %d not in [1, %d]", fn, n, PS_MAX_TASKS);
+  for (int i = 0; i < n; ++i) {
+    if (!h_in[i] || !h_out[i]) return fail(PS_ERR_INVALID_ARG, "%s: null row pointer of task %d", fn, i);
+    if ((reinterpret_cast<uintptr_t>(h_in[i]) | reinterpret_cast<uintptr_t>(h_out[i])) % 16 != 0)
+      return fail(PS_ERR_INVALID_ARG, "%s: rows of task %d not 16-byte aligned", fn, i);
+  }
+  Batch bt;
+  ps_status st = prepare_batch(p, b, te, tasks, n, h_in[0], h_out[0], fn, &bt);
+  if (st) return st;
+  const size_t per = (size_t)p->L() * b->d.hidden;
+  WsPtrs w;
+  if ((st = ws_from_pool(p, ws_sizes(p, b, n), hs, &w))) return st;
+  ps_kv_pool::Workspace* ws = p->workspace(hs);
+  if ((st = ws->h.reserve(sizeof(float) * per * n, hs))) return st;
+  float* h = static_cast<float*>(ws->h.p);
+  if ((st = begin_batch(p, b, te, bt, w, hs))) return st;
+  for (int i = 0; i < n; ++i)
+    PS_HIP(hipMemcpyAsync(h + per * i, h_in[i], sizeof(float) * per, hipMemcpyDeviceToDevice, hs));
+  if ((st = run_stage_all(p, b, w, n, h, h, hs))) return st;
+  for (int i = 0; i < n; ++i)
+    PS_HIP(hipMemcpyAsync(h_out[i], h + per * i, sizeof(float) * per, hipMemcpyDeviceToDevice, hs));
+  commit_writes(p, bt, tasks);
+  return PS_OK;
 }
 
 extern "C" ps_status ps_stage_batch_probe(ps_kv_pool* p, const ps_block* b, ps_time_embed* te,

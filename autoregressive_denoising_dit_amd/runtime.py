@@ -288,6 +288,23 @@ def stage_batch(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], h_in
                                   _stream_ptr(cuda_stream)))
 
 
+def stage_batch_rows(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], h_in: Sequence[torch.Tensor],
+                     h_out: Sequence[torch.Tensor], cuda_stream=None) -> None:
+    """stage_batch on tasks whose rows live in separate tensors: h_in[i],
+    h_out[i] fp32 [L, D] (ps_stage_batch_rows)."""
+    n = len(tasks)
+    if len(h_in) != n or len(h_out) != n:
+        raise ValueError("one input and one output row tensor per task")
+    for i in range(n):
+        _need(h_in[i], torch.float32, (pool.tokens, pool.hidden), f"h_in[{i}]")
+        _need(h_out[i], torch.float32, (pool.tokens, pool.hidden), f"h_out[{i}]")
+    arr = (Task * max(n, 1))(*tasks)
+    pin = (C.c_void_p * n)(*[t.data_ptr() for t in h_in])
+    pout = (C.c_void_p * n)(*[t.data_ptr() for t in h_out])
+    check(pool.lib.ps_stage_batch_rows(pool.handle, block.handle, te.handle, arr, n, pin, pout,
+                                       _stream_ptr(cuda_stream)))
+
+
 def stage_batch_static(pool: Pool, block: Block, te: TimeEmbed, tasks: List[Task], h_in: torch.Tensor,
                        h_out: torch.Tensor, cuda_stream=None) -> None:
     """stage_batch without device allocation (ps_stage_batch_static): the

@@ -218,6 +218,85 @@ def run_placement(cfg, a, b, n_gpus=24, max_discrepancy=2):
     return rows
 
 
+def run_placed_bench(cfg, n_streams=3, ranks_per_stream=4, measured=24, sweep=(1, 2, 4, 8, 12)):
+    """The stage groups the joint placement puts on this GPU, run as the stage
+    pipeline (runner.PlacedRunner): the block-batch cost a + b n is fitted on
+    this GPU first, the placement admits streams on one GPU under an SLO of
+    1.05 x the modelled cycle of n_streams whole streams (so exactly that many
+    fit), and the streams start at offset phases.  After the pipeline has
+    filled, each tick's time is measured and compared with the cycle the
+    placement assumed and with the SLO."""
+    import torch
+    from autoregressive_denoising_dit_amd import runtime
+    from autoregressive_denoising_dit_amd.runner import PlacedRunner, model_cycle_ms, rank_stages
+    from autoregressive_denoising_dit_amd.sched import Scheduler
+    times, a, b = run_batch_sweep(cfg, sizes=sweep)
+    B, S, W, D, F, H, d = cfg.n_blocks, cfg.n_steps, cfg.window, cfg.hidden, cfg.ffn, cfg.heads, cfg.head_dim
+    N = B * S
+    full = {sg: list(range(N)) for sg in range(n_streams)}
+    slo = 1.05 * model_cycle_ms(full, S, a, b)
+    sched = Scheduler(1, 64, B, S, slo, a, b, 2, ranks_per_stream)
+    ranks, sg = [], 0
+    while True:
+        gpus = sched.admit(sg)
+        if gpus is None:
+            break
+        ranks += [(sg, *rank_stages(N, len(gpus), r)) for r in range(len(gpus))]
+        sg += 1
+    admitted = sg
+    _log(f"placed: a = {a:.3f} ms, b = {b:.3f} ms, SLO {slo:.1f} ms, {admitted} stream(s) admitted")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def rn(*shape, dtype=torch.float32, std=0.02):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(dtype).contiguous()
+
+    pool = runtime.Pool(admitted, B, S, W + 1, cfg.grid, H, d, cfg.n_ctx, runtime.ps_dtype(cfg.dtype))
+    blocks, keep = [], []
+    for bi in range(B):
+        w = {"wqkv": rn(3 * D, D, dtype=td), "wo": rn(D, D, dtype=td), "wq2": rn(D, D, dtype=td),
+             "wkv2": rn(2 * D, D, dtype=td), "wo2": rn(D, D, dtype=td), "w1": rn(F, D, dtype=td),
+             "w2": rn(D, F, dtype=td), "bqkv": rn(3 * D), "bo": rn(D), "bq2": rn(D), "bkv2": rn(2 * D),
+             "bo2": rn(D), "b1": rn(F), "b2": rn(D), "tmod": rn(6, D)}
+        blk = runtime.Block(w, D, H, d, F, bi, runtime.ps_dtype(cfg.dtype))
+        for s_ in range(admitted):
+            pool.context_set(blk, s_, rn(cfg.n_ctx, D, dtype=td, std=1.0))
+        blocks.append(blk)
+        keep.append(w)
+    tw = {"wt1": rn(D, 256), "bt1": rn(D), "wt2": rn(D, D), "bt2": rn(D), "wp": rn(6 * D, D), "bp": rn(6 * D)}
+    te = runtime.TimeEmbed(tw, D, capacity=16)
+    starts = {s_: 2 * s_ for s_ in range(admitted)}
+    fill = max(starts.values()) + N - 1          # first tick with every stage busy
+    n_tick = fill + measured
+    n_chunks = n_tick
+    x = {s_: rn(n_chunks, cfg.tokens, D, std=1.0) for s_ in range(admitted)}
+    runner = PlacedRunner(pool, blocks, te, cfg.timesteps, W, ranks, starts, n_chunks)
+    torch.cuda.synchronize()
+    ev = {}
+    for tau in range(n_tick):
+        if tau == fill:
+            ev[tau] = torch.cuda.Event(enable_timing=True)
+            ev[tau].record()
+        runner.run_tick(tau, x)
+        if tau >= fill:
+            ev[tau + 1] = torch.cuda.Event(enable_timing=True)
+            ev[tau + 1].record()
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(v).all().item() for v in x.values()), "non-finite latents"
+    ticks = sorted(ev[t].elapsed_time(ev[t + 1]) for t in range(fill, n_tick))
+    model = runner.model_cycle_ms(a, b)
+    mean = sum(ticks) / len(ticks)
+    return {"batch_ms": {str(n): round(t, 3) for n, t in times.items()},
+            "fit_ms": {"fixed": round(a, 4), "per_task": round(b, 4)},
+            "slo_ms": round(slo, 3), "streams_admitted": admitted, "ranks_per_stream": ranks_per_stream,
+            "start_ticks": starts, "tasks_per_block_batch": runner.tick_blocks[0],
+            "cycle_ms": {"measured_mean": round(mean, 3), "measured_p90": round(ticks[(9 * len(ticks)) // 10], 3),
+                         "model": round(model, 3), "measured_over_model": round(mean / model, 4)},
+            "slo_violations": sum(1 for t in ticks if t > slo), "ticks_measured": len(ticks),
+            "chunk_interval_ms_per_stream": round(mean, 3)}
+
+
 def stage_tasks(cfg, n_tasks, tau, base_chunk=100):
     """Task i: stream i at step (tau + i) mod S, a steady-state chunk with a full window."""
     from autoregressive_denoising_dit_amd import runtime
@@ -449,10 +528,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c5", "c3", "c4", "placement"],
+    ap.add_argument("--workload", default="c5", choices=["c2", "c5", "c3", "c4", "placement", "placed"],
                     help="c5 (default) / c2: one stage batch per step; c3 / c4: the staggered schedule "
                          "over all blocks and steps, reporting the chunk interval; placement: block-batch "
-                         "cost sweep at the 1.3B and 5B shapes and the joint placement it drives")
+                         "cost sweep at the 1.3B and 5B shapes and the joint placement it drives; placed: "
+                         "the stage groups placed on this GPU run as the stage pipeline at the 1.3B shape, "
+                         "measured cycle against the placement's model")
     ap.add_argument("--overlap", type=int, default=1,
                     help="c5 / c2: streams that consecutive stage batches alternate over (1 = one stream)")
     ap.add_argument("--head", action="store_true",
@@ -488,6 +569,17 @@ def main():
                              "placement_24_gpus": run_placement(cfg, a, b)}
         print(json.dumps({"metric": "streams admitted on 24 GPUs, joint placement vs equal split",
                           "n_gpus": 1, "data": "synthetic; batch costs measured on this GPU", **res}), flush=True)
+        return
+    if args.workload == "placed":
+        cfg = get("c3")
+        res = run_placed_bench(cfg)
+        print(json.dumps({"metric": "measured vs modelled cycle of the stage groups placed on one GPU",
+                          "n_gpus": 1, "dtype": cfg.dtype,
+                          "data": "synthetic (seeded random-init weights, N(0,1) latents and contexts)",
+                          "config": {"workload": "placed_wan13b_pipeline", "blocks": cfg.n_blocks,
+                                     "steps": cfg.n_steps, "window": cfg.window, "tokens_per_chunk": cfg.tokens,
+                                     "hidden": cfg.hidden},
+                          **res}), flush=True)
         return
     if args.workload in ("c3", "c4"):
         cfg = get(args.workload)

@@ -234,6 +234,18 @@ ps_status ps_stage_batch(ps_kv_pool* pool, const ps_block* block, ps_time_embed*
                          const ps_task* tasks, int32_t n_tasks, const float* h_in,
                          float* h_out, hipStream_t hs);
 
+/* ps_stage_batch for a batch whose tasks' hidden states are not one contiguous
+ * slice: a GPU that hosts stage groups of several streams forms each block's
+ * batch from whichever of their tasks are ready (163.com release, bullets
+ * "时分复用" and "虚拟 rank 的动态放置", Fig. 3 right).  h_in[i], h_out[i]:
+ * device fp32 [L, D] rows of task i (host arrays of n_tasks pointers, each
+ * 16-byte aligned; h_in[i] == h_out[i] allowed, distinct tasks' rows must not
+ * overlap).  The rows are gathered into the stream's workspace, run as one
+ * batch and scattered back.  Errors as ps_stage_batch. */
+ps_status ps_stage_batch_rows(ps_kv_pool* pool, const ps_block* block, ps_time_embed* te,
+                              const ps_task* tasks, int32_t n_tasks, const float* const* h_in,
+                              float* const* h_out, hipStream_t hs);
+
 /* ps_stage_batch for callers that cannot allocate device memory (code under
  * HIP graph capture, serving loops and harnesses that forbid hipMalloc).  Same
  * arguments, results and errors as ps_stage_batch; it neither allocates nor
