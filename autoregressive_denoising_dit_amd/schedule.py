@@ -63,10 +63,19 @@ def n_ticks(n_chunks: int, n_steps: int, k: int) -> int:
 
 
 class StaggeredRunner:
-    """Runs the staggered schedule of `n_chunks` chunks of `n_streams` streams."""
+    """Runs the staggered schedule of `n_chunks` chunks of `n_streams` streams.
+
+    groups > 1 splits each tick's tasks into that many groups of consecutive
+    steps (the tick's task list is ordered by chunk, so each group is a
+    contiguous slice of the latents).  The groups share no dependency inside a
+    tick -- a task reads the noisy KV of its own step and its own hidden state
+    -- so their block batches run concurrently on separate HIP streams, one
+    group's partial rounds of tiles overlapping the other's work; the tick ends
+    when every group has finished.  A task's results do not depend on its batch
+    companions, so the grouping changes no result."""
 
     def __init__(self, pool: Pool, blocks: Sequence[Block], te: TimeEmbed, timesteps: Sequence[float],
-                 window: int, k: int, n_streams: int, head: Optional[Head] = None):
+                 window: int, k: int, n_streams: int, head: Optional[Head] = None, groups: int = 1):
         if pool.n_slots < window + k:
             raise ValueError(f"ring of {pool.n_slots} slots is smaller than window + k = {window + k}")
         if head is not None and head.hidden != pool.hidden:
@@ -79,6 +88,12 @@ class StaggeredRunner:
         rows = self.S * k * n_streams * self.L
         self.hbuf = torch.empty((rows, self.D), dtype=torch.float32, device="cuda")
         self.vbuf = torch.empty((rows, self.P), dtype=torch.float32, device="cuda") if head is not None else None
+        if not 1 <= groups <= min(self.S, 4):
+            raise ValueError(f"groups must be in [1, {min(self.S, 4)}]")
+        if groups > 1 and head is not None:
+            raise ValueError("the head's workspace serves one stream: groups > 1 needs head=None")
+        self.groups = groups
+        self.side = [torch.cuda.Stream() for _ in range(groups - 1)]
 
     def tasks_for(self, tau: int, n_chunks: int):
         tl = tick_tasks(tau, n_chunks, self.S, self.k, self.n_streams)
@@ -90,28 +105,57 @@ class StaggeredRunner:
                                               [(c - nr + i) % R for i in range(nr)]))
         return tl, ps_tasks
 
+    def _run_group(self, tl, tasks, x, row0, cuda_stream):
+        """All blocks, then the head and Euler, for one group of the tick's
+        tasks (rows row0 .. of the tick's slice)."""
+        c_lo = tl[0][1]
+        n = len(tl)
+        rows = n * self.L
+        xs = x[c_lo:c_lo + n // self.n_streams].view(rows, self.P)
+        h = self.hbuf[row0:row0 + rows]
+        if self.head is not None:
+            runtime.patch_embed(self.head, xs, h, cuda_stream=cuda_stream)
+        for b, blk in enumerate(self.blocks):
+            runtime.stage_batch(self.pool, blk, self.te, tasks, xs if (b == 0 and self.head is None) else h, h,
+                                cuda_stream=cuda_stream)
+        steps = [s for (_, _, s) in tl]
+        if self.head is not None:
+            v = self.vbuf[row0:row0 + rows]
+            runtime.output_head(self.head, self.te, [self.ts[s] for s in steps], self.L, h, v, cuda_stream=cuda_stream)
+            runtime.euler_update_steps(xs, v, self.ts[:-1], steps, self.L, self.P, cuda_stream=cuda_stream)
+        else:
+            runtime.euler_update_steps(xs, h, self.ts[:-1], steps, self.L, self.D, cuda_stream=cuda_stream)
+
     def run_tick(self, tau: int, x: torch.Tensor, n_chunks: int):
         """x: fp32 [n_chunks, n_streams, L, P] latents (P = D without a head),
         updated in place."""
         tl, tasks = self.tasks_for(tau, n_chunks)
         if not tl:
             return tl
-        c_lo = tl[0][1]
-        n = len(tl)
-        rows = n * self.L
-        xs = x[c_lo:c_lo + n // self.n_streams].view(rows, self.P)
-        h = self.hbuf[:rows]
-        if self.head is not None:
-            runtime.patch_embed(self.head, xs, h)
-        for b, blk in enumerate(self.blocks):
-            runtime.stage_batch(self.pool, blk, self.te, tasks, xs if (b == 0 and self.head is None) else h, h)
-        steps = [s for (_, _, s) in tl]
-        if self.head is not None:
-            v = self.vbuf[:rows]
-            runtime.output_head(self.head, self.te, [self.ts[s] for s in steps], self.L, h, v)
-            runtime.euler_update_steps(xs, v, self.ts[:-1], steps, self.L, self.P)
-        else:
-            runtime.euler_update_steps(xs, h, self.ts[:-1], steps, self.L, self.D)
+        if self.groups == 1:
+            self._run_group(tl, tasks, x, 0, None)
+            return tl
+        # split by step into groups of whole steps (each a run of consecutive
+        # chunks); group 0 on the current stream, the others on side streams
+        steps = sorted({s for (_, _, s) in tl}, reverse=True)
+        per = -(-len(steps) // self.groups)
+        parts = [set(steps[i:i + per]) for i in range(0, len(steps), per)]
+        main = torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(main)
+        row0 = 0
+        for gi, part in enumerate(parts):
+            idx = [i for i, t in enumerate(tl) if t[2] in part]
+            sub_tl, sub_tasks = [tl[i] for i in idx], [tasks[i] for i in idx]
+            st = main if gi == 0 else self.side[gi - 1]
+            if gi > 0:
+                st.wait_event(start)
+            self._run_group(sub_tl, sub_tasks, x, row0, None if gi == 0 else st)
+            row0 += len(idx) * self.L
+        for st in self.side[:len(parts) - 1]:
+            done = torch.cuda.Event()
+            done.record(st)
+            main.wait_event(done)
         return tl
 
     def run(self, x: torch.Tensor, n_chunks: int, on_tick: Optional[Callable[[int, list], None]] = None):

@@ -94,7 +94,7 @@ def setup_stage(cfg, n_tasks, seed=0):
     return dict(pool=pool, blk=blk, te=te, x=x, h=h, xe=xe, w=w, tw=tw)
 
 
-def run_stagger_bench(cfg, measured=64, with_head=False):
+def run_stagger_bench(cfg, measured=64, with_head=False, groups=1):
     """Steady-state chunk interval of one stream under the staggered schedule
     (all blocks, all steps, k chunks per step per tick): `measured` chunks
     completed after a warm-up of S + W + 2 ticks, from events recorded after
@@ -132,7 +132,7 @@ def run_stagger_bench(cfg, measured=64, with_head=False):
         P = cfg.latent_dim
         head = runtime.Head({"w_embed": rn(D, P, dtype=td), "w_head": rn(P, D, dtype=td), "b_embed": rn(D),
                              "b_head": rn(P), "t_head": rn(2, D)}, D, P, runtime.ps_dtype(cfg.dtype))
-    runner = StaggeredRunner(pool, blocks, te, cfg.timesteps, W, k, 1, head=head)
+    runner = StaggeredRunner(pool, blocks, te, cfg.timesteps, W, k, 1, head=head, groups=groups)
     tau0 = S + W + 2                       # warm-up ticks (pipeline filled, full windows)
     tau1 = tau0 + (measured + k - 1) // k  # each later tick completes k chunks
     tau2 = tau1 + (tau1 - tau0)            # then as many ticks again with per-kernel events
@@ -536,6 +536,10 @@ def main():
                          "measured cycle against the placement's model")
     ap.add_argument("--overlap", type=int, default=1,
                     help="c5 / c2: streams that consecutive stage batches alternate over (1 = one stream)")
+    ap.add_argument("--no-timeshared", action="store_true",
+                    help="c5: leave out the c3 / c4 chunk intervals that the default line also carries")
+    ap.add_argument("--groups", type=int, default=2,
+                    help="c3 / c4: run each tick's tasks as this many groups of steps on concurrent streams")
     ap.add_argument("--head", action="store_true",
                     help="c3 / c4: run on latent patches with the patch embedding and output head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -583,7 +587,7 @@ def main():
         return
     if args.workload in ("c3", "c4"):
         cfg = get(args.workload)
-        interval, tick, done, per_tick = run_stagger_bench(cfg, with_head=args.head)
+        interval, tick, done, per_tick = run_stagger_bench(cfg, with_head=args.head, groups=args.groups)
         per_chunk = cfg.n_blocks * cfg.n_steps * stage_flops(cfg, cfg.window)
         print(json.dumps({
             "metric": "steady-state chunk interval (ms), staggered schedule, one stream",
@@ -591,7 +595,8 @@ def main():
             "dtype": cfg.dtype, "data": "synthetic (seeded random-init weights, N(0,1) latents and contexts)",
             "config": {"workload": cfg.name, "blocks": cfg.n_blocks, "steps": cfg.n_steps, "k": cfg.k,
                        "window": cfg.window, "tokens_per_chunk": cfg.tokens, "hidden": cfg.hidden,
-                       "head": bool(args.head), "latent_dim": cfg.latent_dim if args.head else None},
+                       "head": bool(args.head), "latent_dim": cfg.latent_dim if args.head else None,
+                       "groups": args.groups},
             "chunks_measured": done, "tick_ms": round(tick, 3),
             "stage_tasks_per_s": round(cfg.n_blocks * cfg.n_steps * cfg.k / (tick * 1e-3), 1),
             "mfma_frac": round(per_chunk / (interval * 1e-3) / PEAK[cfg.dtype], 4),
@@ -657,6 +662,17 @@ def main():
         "kernels": kernels,
         "roofline": roof,
     }
+    if args.workload == "c5" and not args.no_timeshared:
+        # the time-shared configurations, measured after the timed steps: the
+        # staggered schedule over all blocks and steps of one stream
+        for name in ("c3", "c4"):
+            tcfg = get(name)
+            _log(f"time-shared {name}: staggered schedule, {args.groups} group(s)")
+            interval, tick, done, _ = run_stagger_bench(tcfg, measured=32, groups=args.groups)
+            per_chunk = tcfg.n_blocks * tcfg.n_steps * stage_flops(tcfg, tcfg.window)
+            out[f"{name}_chunk_interval_ms"] = round(interval, 3)
+            out[f"{name}_mfma_frac"] = round(per_chunk / (interval * 1e-3) / PEAK[tcfg.dtype], 4)
+        out["timeshared_groups"] = args.groups
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, n_read)
     print(json.dumps(out), flush=True)

@@ -356,7 +356,7 @@ def _schedule_inputs(cfg, n_chunks, n_streams, seed=0):
     return blocks, tw, ctxs, lat
 
 
-def _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, n_streams, k, keep_pool=False):
+def _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, n_streams, k, keep_pool=False, groups=1):
     from autoregressive_denoising_dit_amd.schedule import StaggeredRunner
     td = runtime.TORCH_DTYPE[runtime.ps_dtype(cfg.dtype)]
     pool = make_pool(cfg, n_streams=n_streams, n_blocks=cfg.n_blocks, n_slots=cfg.window + k)
@@ -367,7 +367,7 @@ def _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, n_streams, k, keep_pool=
             pool.context_set(blk, sg, to_dev(ctxs[sg], td))
     x = torch.stack([torch.stack([to_dev(lat[(sg, c)], torch.float32) for sg in range(n_streams)])
                      for c in range(n_chunks)]).contiguous()
-    run = StaggeredRunner(pool, blks, te, cfg.timesteps, cfg.window, k, n_streams)
+    run = StaggeredRunner(pool, blks, te, cfg.timesteps, cfg.window, k, n_streams, groups=groups)
     run.run(x, n_chunks)
     torch.cuda.synchronize()
     return (host(x), pool) if keep_pool else host(x)
@@ -434,6 +434,28 @@ def test_schedule_bf16_c3_shape_matches_oracle():
                 ek, ev = rel_err(host(kg), kr), rel_err(host(vg), vr)
                 say(f"block {b} step {s} slot {slot} (chunk {chunk}): k err {ek:.2e}, v err {ev:.2e}")
                 assert ek <= t and ev <= t
+
+
+def test_schedule_groups_on_concurrent_streams_bitwise():
+    """A tick's tasks split into two groups of steps on two HIP streams give
+    bitwise the latents of one batch per block (1.3B width, 2 blocks, k = 2,
+    6 chunks); and at the tiny fp32 shape they match the sequential oracle."""
+    cfg = with_(C3, n_blocks=2)
+    n_chunks = 6
+    blocks, tw, ctxs, lat = _schedule_inputs(cfg, n_chunks, 1)
+    say("schedule groups 1 vs 2, 1.3B width")
+    a = _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, 1, 2, groups=1)
+    b = _gpu_schedule(cfg, blocks, tw, ctxs, lat, n_chunks, 1, 2, groups=2)
+    assert np.array_equal(a, b) and np.all(np.isfinite(a))
+    cfg = C1
+    blocks, tw, ctxs, lat = _schedule_inputs(cfg, 4, 2)
+    gx = _gpu_schedule(cfg, blocks, tw, ctxs, lat, 4, 2, 2, groups=2)
+    ox, _ = oracle.run_schedule(cfg, blocks, tw, lambda sg, c: lat[(sg, c)], ctxs, 4, order="sequential")
+    for c in range(4):
+        for sg in range(2):
+            e = rel_err(gx[c, sg], ox[(sg, c)])
+            say(f"groups 2, chunk {c} stream {sg}: x^S err {e:.2e}")
+            assert e <= 1e-4
 
 
 # ------------------------------------------------- patch embedding / head
