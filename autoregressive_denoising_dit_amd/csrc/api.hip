@@ -463,6 +463,16 @@ extern "C" ps_status ps_block_destroy(ps_block* b) {
   return PS_OK;
 }
 
+// Whether hs is capturing into a HIP graph.
+static bool capturing(hipStream_t hs) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(hs, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
 // ------------------------------------------------------ timestep embedding
 static void te_free(ps_time_embed* te) {
   if (te->cache) (void)hipFree(te->cache);
@@ -560,6 +570,15 @@ static ps_status te_resolve(ps_time_embed* te, const float* t, int n, hipStream_
   }
   if ((int)keys.size() > cap)
     return fail(PS_ERR_INVALID_ARG, "time embed: %d distinct timesteps in one call, capacity %d", (int)keys.size(), cap);
+  // Under graph capture every row must already be cached and nothing waits
+  // on or records events outside the graph.
+  const bool cap_mode = capturing(hs);
+  if (cap_mode)
+    for (uint32_t k : keys) {
+      bool hit = false;
+      for (int j = 0; j < cap; ++j) hit |= te->valid[j] && te->key[j] == k;
+      if (!hit) return fail(PS_ERR_UNSUPPORTED, "time embed: a timestep is not cached; fill it before graph capture");
+    }
   ps_status st = te_stream_slot(te, hs, slot);
   if (st) return st;
   const int D = te->d.hidden;
@@ -571,7 +590,7 @@ static ps_status te_resolve(ps_time_embed* te, const float* t, int n, hipStream_
     for (int j = 0; j < cap && row < 0; ++j)
       if (te->valid[j] && te->key[j] == k) row = j;
     if (row >= 0) {
-      if (te->fill_stream[row] != hs) PS_HIP(hipStreamWaitEvent(hs, te->fill_ev[row], 0));
+      if (te->fill_stream[row] != hs && !cap_mode) PS_HIP(hipStreamWaitEvent(hs, te->fill_ev[row], 0));
     } else {
       int victim = -1;
       for (int j = 0; j < cap; ++j) {
@@ -606,7 +625,9 @@ static ps_status te_resolve(ps_time_embed* te, const float* t, int n, hipStream_
 }
 
 // After the kernels that read rows[0 .. n-1] have been enqueued on hs.
+// Reads inside a captured graph are not tracked (no event outside the graph).
 static ps_status te_mark_read(ps_time_embed* te, const int* rows, int n, int slot, hipStream_t hs) {
+  if (capturing(hs)) return PS_OK;
   PS_HIP(hipEventRecord(te->rd_ev[slot], hs));
   for (int i = 0; i < n; ++i) te->readers[rows[i]] |= 1u << slot;
   return PS_OK;
@@ -821,6 +842,9 @@ static ps_status ws_from_pool(ps_kv_pool* p, const WsSizes& z, hipStream_t hs, W
   if (!w)
     return fail(PS_ERR_INVALID_ARG, "ps_stage_batch: more than %d streams use this pool", PS_MAX_STREAMS_PER_POOL);
   DevBuf* bufs[7] = {&w->mod, &w->rope, &w->y, &w->q, &w->a, &w->u, &w->tasks};
+  for (int i = 0; i < 7; ++i)
+    if (z.b[i] > bufs[i]->bytes && capturing(hs))
+      return fail(PS_ERR_UNSUPPORTED, "ps_stage_batch: the workspace of this stream must grow; size it before graph capture");
   for (int i = 0; i < 7; ++i) {
     ps_status st = bufs[i]->reserve(z.b[i], hs);
     if (st) return st;

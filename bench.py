@@ -297,6 +297,81 @@ def run_placed_bench(cfg, n_streams=3, ranks_per_stream=4, measured=24, sweep=(1
             "chunk_interval_ms_per_stream": round(mean, 3)}
 
 
+def run_graph_bench(cfg, reps=50):
+    """One step of the path -- at c2 a stage batch and its Euler update, at
+    c3 / c4 one steady-state tick of the staggered schedule (all blocks, then
+    Euler) -- run eagerly and as a HIP graph captured once and replayed, the
+    same work each time, on one stream set up by an uncaptured warm-up."""
+    import torch
+    from autoregressive_denoising_dit_amd import runtime
+    stream = torch.cuda.Stream()
+    if cfg.n_blocks == 1:
+        st = setup_stage(cfg, cfg.batch)
+        tl = stage_tasks(cfg, cfg.batch, 0)
+        dts = [cfg.timesteps[t.step] - (cfg.timesteps[t.step + 1] if t.step + 1 < cfg.n_steps else 0.0) for t in tl]
+
+        def step():
+            runtime.stage_batch(st["pool"], st["blk"], st["te"], tl, st["x"], st["h"])
+            runtime.euler_update(st["xe"], st["h"], dts, cfg.tokens, cfg.hidden)
+        keep = st
+    else:
+        from autoregressive_denoising_dit_amd.schedule import StaggeredRunner
+        g_ = torch.Generator(device="cuda")
+        g_.manual_seed(0)
+        td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        D, F, H, d, B, S, W, k = cfg.hidden, cfg.ffn, cfg.heads, cfg.head_dim, cfg.n_blocks, cfg.n_steps, cfg.window, cfg.k
+
+        def rn(*shape, dtype=torch.float32, std=0.02):
+            return (torch.randn(*shape, generator=g_, device="cuda") * std).to(dtype).contiguous()
+        pool = runtime.Pool(1, B, S, W + k, cfg.grid, H, d, cfg.n_ctx, runtime.ps_dtype(cfg.dtype), check_slots=False)
+        blocks, ws = [], []
+        for b in range(B):
+            w = {"wqkv": rn(3 * D, D, dtype=td), "wo": rn(D, D, dtype=td), "wq2": rn(D, D, dtype=td),
+                 "wkv2": rn(2 * D, D, dtype=td), "wo2": rn(D, D, dtype=td), "w1": rn(F, D, dtype=td),
+                 "w2": rn(D, F, dtype=td), "bqkv": rn(3 * D), "bo": rn(D), "bq2": rn(D), "bkv2": rn(2 * D),
+                 "bo2": rn(D), "b1": rn(F), "b2": rn(D), "tmod": rn(6, D)}
+            blk = runtime.Block(w, D, H, d, F, b, runtime.ps_dtype(cfg.dtype))
+            pool.context_set(blk, 0, rn(cfg.n_ctx, D, dtype=td, std=1.0))
+            blocks.append(blk)
+            ws.append(w)
+        tw = {"wt1": rn(D, 256), "bt1": rn(D), "wt2": rn(D, D), "bt2": rn(D), "wp": rn(6 * D, D), "bp": rn(6 * D)}
+        te = runtime.TimeEmbed(tw, D, capacity=16)
+        runner = StaggeredRunner(pool, blocks, te, cfg.timesteps, W, k, 1)
+        tau = S + W + 2
+        n_chunks = k * (tau + 1)
+        x = rn(n_chunks, 1, cfg.tokens, D, std=1.0)
+
+        def step():
+            runner.run_tick(tau, x, n_chunks)
+        keep = (pool, blocks, ws, te, runner, x)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):          # warm-up: workspaces and timestep rows on this stream
+            step()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) / reps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    replay = e0.elapsed_time(e1) / reps
+    del keep
+    return {"eager_ms": round(eager, 4), "graph_ms": round(replay, 4), "graph_over_eager": round(replay / eager, 4),
+            "reps": reps}
+
+
 def stage_tasks(cfg, n_tasks, tau, base_chunk=100):
     """Task i: stream i at step (tau + i) mod S, a steady-state chunk with a full window."""
     from autoregressive_denoising_dit_amd import runtime
@@ -536,6 +611,8 @@ def main():
                          "measured cycle against the placement's model")
     ap.add_argument("--overlap", type=int, default=1,
                     help="c5 / c2: streams that consecutive stage batches alternate over (1 = one stream)")
+    ap.add_argument("--graph", action="store_true",
+                    help="c2 / c3 / c4: time one step (c2) or one tick (c3, c4) eagerly and as a replayed HIP graph")
     ap.add_argument("--no-timeshared", action="store_true",
                     help="c5: leave out the c3 / c4 chunk intervals that the default line also carries")
     ap.add_argument("--groups", type=int, default=2,
@@ -573,6 +650,13 @@ def main():
                              "placement_24_gpus": run_placement(cfg, a, b)}
         print(json.dumps({"metric": "streams admitted on 24 GPUs, joint placement vs equal split",
                           "n_gpus": 1, "data": "synthetic; batch costs measured on this GPU", **res}), flush=True)
+        return
+    if args.graph:
+        cfg = get(args.workload)
+        res = run_graph_bench(cfg)
+        print(json.dumps({"metric": "one step as a HIP graph vs eager launches", "n_gpus": 1, "dtype": cfg.dtype,
+                          "config": {"workload": cfg.name, "unit": "stage step" if cfg.n_blocks == 1 else "tick"},
+                          **res}), flush=True)
         return
     if args.workload == "placed":
         cfg = get("c3")

@@ -34,6 +34,13 @@
  *    the row it replaces, and a call on another stream that reads the row
  *    waits on the device for the fill.  No call waits on the host, except
  *    the *_destroy calls, ps_kv_pool_release_stream and ps_trace_enable.
+ *  - Calls that launch work may be captured into a HIP graph on a stream
+ *    that an earlier, uncaptured call has set up: the timestep rows a call
+ *    reads must already be cached and the stream's workspace large enough
+ *    (else PS_ERR_UNSUPPORTED, nothing enqueued).  Reads of cached rows inside
+ *    a graph are not tracked, so a graph must not be replayed after a row it
+ *    reads has been replaced (keep the cache's capacity above the timesteps
+ *    in use).  The arguments of a captured call are fixed in the graph.
  *  - A failing call enqueues nothing, with one exception: a HIP runtime
  *    failure part-way through a call's launches (PS_ERR_HIP) may leave the
  *    launches before it enqueued.

@@ -458,6 +458,84 @@ def test_schedule_groups_on_concurrent_streams_bitwise():
             assert e <= 1e-4
 
 
+@pytest.mark.parametrize("cfg", [C1, with_(C2, hidden=512, heads=8, head_dim=64, ffn=1024, n_ctx=200)],
+                         ids=["tiny_fp32", "bf16_d64"])
+def test_stage_step_replays_as_a_graph(cfg):
+    """A stage batch and its Euler update captured into a HIP graph (on a
+    stream an uncaptured call set up) and replayed three times, with eager
+    work and synchronisations between the replays: every replay gives bitwise
+    the eager call's output, latents and cache entries."""
+    tasks = [(0, 5, 1, 2), (1, 4, 0, 2)]
+    case = StageCase(cfg, tasks, n_slots=cfg.window + 2)
+    ps_tasks = case.setup_gpu()
+    h_in = to_dev(case.h_in, torch.float32)
+    h_out = torch.empty_like(h_in)
+    x0 = to_dev(inputs.hidden_rows(cfg, len(tasks), 0, tag="x0"), torch.float32)
+    x = x0.clone()
+    dts = [0.5, 0.25]
+    stream = torch.cuda.Stream()
+    say("graph replay", cfg.name)
+
+    def step():
+        runtime.stage_batch(case.pool, case.block, case.te, ps_tasks, h_in, h_out)
+        runtime.euler_update(x, h_out, dts, cfg.tokens, cfg.hidden)
+
+    with torch.cuda.stream(stream):
+        step()
+        x.copy_(x0)
+        step()
+    torch.cuda.synchronize()
+    ref_h, ref_x = host(h_out), host(x)
+    ref_kv = [host(t) for (sg, c, s_, _) in tasks for t in case.pool.fetch(sg, 0, s_, c % case.R)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    for rep in range(3):
+        # eager work between replays: a plain call on other buffers
+        other = torch.zeros_like(h_in)
+        runtime.stage_batch(case.pool, case.block, case.te, ps_tasks, h_in, other)
+        torch.cuda.synchronize()
+        h_out.fill_(float("nan"))
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(h_out), ref_h), rep
+        assert np.array_equal(host(x), ref_x), rep
+        kv = [host(t) for (sg, c, s_, _) in tasks for t in case.pool.fetch(sg, 0, s_, c % case.R)]
+        assert all(np.array_equal(a, b) for a, b in zip(kv, ref_kv)), rep
+
+
+def test_capture_refuses_uncached_timestep_and_workspace_growth():
+    """Under capture a call that would fill a timestep row or grow the
+    stream's workspace is refused (PS_ERR_UNSUPPORTED) instead of enqueuing
+    that work into the graph; the stream keeps working afterwards."""
+    cfg = C1
+    case = StageCase(cfg, [(0, 3, 1, 2), (0, 2, 1, 2)], n_slots=cfg.window + 2)
+    ps_tasks = case.setup_gpu()
+    L = cfg.tokens
+    h = to_dev(case.h_in, torch.float32)
+    one = h[:L]
+    stream = torch.cuda.Stream()
+    say("capture refusals")
+    with torch.cuda.stream(stream):      # one task at step 1: workspace for one task, row t_1 cached
+        runtime.stage_batch(case.pool, case.block, case.te, ps_tasks[1:], one, one)
+    torch.cuda.synchronize()
+    t0_task = runtime.make_task(0, 0, 0, cfg.timesteps[0], 0, [])   # step 0: its timestep is not cached
+    for tasks, x, why in (([t0_task], one, "timestep"), (ps_tasks, h, "workspace")):
+        graph = torch.cuda.CUDAGraph()
+        with pytest.raises(PsError) as ei:
+            with torch.cuda.graph(graph, stream=stream):
+                runtime.stage_batch(case.pool, case.block, case.te, tasks, x, x)
+        assert ei.value.status == _lib.PS_ERR_UNSUPPORTED and why in str(ei.value), str(ei.value)
+        torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        runtime.stage_batch(case.pool, case.block, case.te, ps_tasks, h, h)
+    torch.cuda.synchronize()
+    assert torch.isfinite(h).all()
+
+
 # ------------------------------------------------- patch embedding / head
 @pytest.mark.parametrize("cfg", [C1, C3, C4], ids=lambda c: c.name)
 def test_patch_embed_and_output_head(cfg):
