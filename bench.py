@@ -534,6 +534,37 @@ def pmc_summary(dirs):
     print(json.dumps(out, indent=1, sort_keys=True), flush=True)
 
 
+def trace_summary(dirs):
+    """Per-kernel dispatch counts and durations from rocprofv3 --kernel-trace
+    CSV output (the kernel_trace.csv of each directory).  Self- and
+    cross-attention share one kernel; within a stage call the self-attention
+    launch comes first, so attention dispatches alternate."""
+    import csv
+    import glob
+    rows = []
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    out = {}
+    attn_seen = 0
+    for (t0, t1, name) in rows:
+        k = _short_kernel(name) or name[:60]
+        if k == "k_gemm" and "Li" in name:
+            k = "k_gemm_E" + name.split("Li", 1)[1][:1]
+        if k == "k_attn":
+            k = "attn_self" if attn_seen % 2 == 0 else "attn_cross"
+            attn_seen += 1
+        agg = out.setdefault(k, {"dispatches": 0, "total_ms": 0.0})
+        agg["dispatches"] += 1
+        agg["total_ms"] += (t1 - t0) * 1e-6
+    for agg in out.values():
+        agg["avg_ms"] = round(agg["total_ms"] / agg["dispatches"], 4)
+        agg["total_ms"] = round(agg["total_ms"], 3)
+    print(json.dumps(out, indent=1, sort_keys=True), flush=True)
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None when there is none or the kernel's source changed since it was taken."""
@@ -624,9 +655,14 @@ def main():
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="only summarise rocprofv3 --pmc CSV output per kernel and exit")
+    ap.add_argument("--trace-summary", nargs="+", metavar="DIR",
+                    help="only summarise rocprofv3 --kernel-trace CSV output per kernel and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
