@@ -665,7 +665,7 @@ def main():
         trace_summary(args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        print("bench.py: the stage path runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -13,8 +13,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 Parity status: every function is pinned by a ``-m "not gpu"`` test against a
 closed form, a library routine, brute force or an invariant (see
 ``tests/test_oracle_*.py``).  The absolute values of a whole block are fixed
-only by the readings of the pages listed in the design notes; the pages print
-no worked numeric example of the block.
+only by the readings taken where the pages are silent (block layout,
+normalisation, modulation, RoPE split, precisions), which the docstrings of
+``block.py`` and ``head.py`` state; the pages print no worked numeric example
+of the block.
 """
 from .block import (  # noqa: F401
     adaln, attention, block_task, context_kv, cross_q, ffn_hidden, gelu_tanh, layer_norm,

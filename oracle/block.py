@@ -13,8 +13,8 @@ but print no formulas:
 The block internals therefore take the plainest reading of a Wan-style DiT
 block: AdaLN-modulated self-attention with 3D RoPE and a gate, cross-attention
 to conditioning tokens, and an AdaLN-modulated GELU-tanh FFN with a gate, with
-6-way modulation from a timestep embedding.  Each reading is listed in the
-design notes.
+6-way modulation from a timestep embedding.  Each function's docstring
+states the reading it takes.
 
 Everything here is float64 and processes one task at a time.  Tensors:
 h [L, D] residual stream; q, k, v [L, H, d]; weights [in, out] (y = x @ W + b).

@@ -9,7 +9,7 @@ the Euler step subtracts.  Sources: the pages evaluate Wan-family backbones
 (AREX feed article on the PhysisServe report, section "实测数字") and cut the
 latent video into chunks of one latent frame; a 60 x 104 latent frame in 2 x 2
 patches is the 30 x 52 token grid of a chunk.  The pages print neither layer,
-so both take the plainest Wan-style reading (design notes, readings R24-R27):
+so both take the plainest Wan-style reading:
 
   * the latent of a chunk is carried patchified, x in R^{L x P} with
     P = C * pf * ph * pw (C latent channels, patch pf x ph x pw); token n is

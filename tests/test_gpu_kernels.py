@@ -11,7 +11,7 @@ seeded entries and the oracle's own keys/values of the batch's chunks
 (rounded), loaded into the pool.  Cross-attention reads the oracle's context
 keys/values (rounded), loaded with ps_context_load.
 
-Bar (reading R21): max|err| / RMS(ref) <= 3e-2 in bf16, <= 1e-4 in fp32, on
+Bar: max|err| / RMS(ref) <= 3e-2 in bf16, <= 1e-4 in fp32, on
 every row of every checked task.  Two allowances, both the storage rounding of
 the kernel's own output and nothing else: an output stored in bf16 (fp32) is
 at most 2^-8 (2^-24) of its value away from the value it rounds, so that much

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 def _check_case(case, task_ids=None, rows=None, delta=True):
     """The stage output h_out and the cache entries written, at the bound
-    (north_star's "output"); with ``delta`` also the branch delta h_out - h_in,
+    (the bound is stated for outputs); with ``delta`` also the branch delta h_out - h_in,
     which is small next to the residual stream."""
     cfg, L = case.cfg, case.cfg.tokens
     t = tol(cfg)
