@@ -145,6 +145,13 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
       lane_off[i] = (uint32_t)(((size_t)f * seg_stride + c * VEC) * sizeof(T));
     }
   }
+  // this wave's copy blocks: all K or all V^T (KB is a multiple of DPW)
+  static_assert(KB % DPW == 0, "a wave's copy blocks must not straddle K and V^T");
+  const bool k_wave = wave * DPW < KB;
+  const size_t my_off = k_wave ? k_off : v_off;
+  const uint32_t my_step = k_wave ? HD * sizeof(T) : sizeof(T);   // bytes per key
+  const uint32_t my_dst = (uint32_t)__builtin_amdgcn_readfirstlane(
+      k_wave ? wave * DPW * 1024 : KT * KCH * 16 + (wave * DPW - KB) * 1024);
   const T* cur_base = seg_base(0);   // base of segment f_seg
   auto copy_tile = [&](int tile) {
     const int t0 = tile * KT;
@@ -152,17 +159,15 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
     const int split = seg_len - f_off;   // tile-relative key where the next segment starts
     const uint32_t stage = lds0 + (uint32_t)((tile % NSTG) * TILE_CH * 16);
     if (split >= KT && t0 + KT <= n_keys) {
-      // buffer resources over this head's K and V^T of the segment; the tile
-      // offset goes in the scalar offset, the lane's in the 32-bit vector one
-      const i32x4 rk = make_rsrc(b0 + k_off, 0xffffffffu), rv = make_rsrc(b0 + v_off, 0xffffffffu);
-      const uint32_t sk = (uint32_t)f_off * HD * sizeof(T), sv = (uint32_t)f_off * sizeof(T);
+      // a buffer resource over this head's K (or V^T) of the segment; the tile
+      // offset goes in the scalar offset, the lane's in the 32-bit vector one.
+      // A wave copies K blocks only or V^T blocks only, so the copies of a
+      // tile are straight-line code.
+      const i32x4 rs = make_rsrc(b0 + my_off, 0xffffffffu);
+      const uint32_t so = (uint32_t)f_off * my_step;
+      const uint32_t d0 = stage + my_dst;
 #pragma unroll
-      for (int i = 0; i < DPW; ++i) {
-        const int bi = wave * DPW + i;   // wave-uniform
-        const uint32_t dst = stage + (bi < KB ? bi * 1024 : KT * KCH * 16 + (bi - KB) * 1024);
-        if (bi < KB) lds_dma16_buf(rk, lane_off[i], sk, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
-        else lds_dma16_buf(rv, lane_off[i], sv, (uint32_t)__builtin_amdgcn_readfirstlane(dst));
-      }
+      for (int i = 0; i < DPW; ++i) lds_dma16_buf(rs, lane_off[i], so, d0 + i * 1024);
     } else {
       const T* b1 = seg_base(min(f_seg + 1, n_seg - 1));
 #pragma unroll
@@ -223,14 +228,28 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
     if (wave_active) {
     // S^T - m for the 64 keys of this tile (the accumulators start at -m)
     f32x16 s[2];
+    s[0] = negm;
+    s[1] = negm;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = negm;
+    for (int u = 0; u < NU_QK; ++u)
 #pragma unroll
-      for (int u = 0; u < NU_QK; ++u) {
+      for (int t = 0; t < 2; ++t) {
         const u32x4 kf = ks[(t * 32 + l32) * KCH + ((2 * u + g) ^ lds_swz<KCH>(l32))];
         Mfma<T>::unit(s[t], kf, qf[u]);
       }
+    if constexpr (kBf16) {
+      // keep KLA key-fragment reads in flight ahead of the MFMAs: the reads
+      // first, then one MFMA per read, then the last KLA MFMAs (left to
+      // itself the scheduler issues each read right before its MFMA, which
+      // then waits the full LDS latency)
+      constexpr int NM = 2 * NU_QK, KLA = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, KLA, 0);
+#pragma unroll
+      for (int i = 0; i < NM - KLA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KLA, 0);
     }
     if ((tile + 1) * KT > n_keys) {   // ragged last tile
 #pragma unroll
@@ -306,6 +325,17 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
         const u32x4 vf = vs[f * VCH + ((2 * u + g) ^ lds_swz<VCH>(f))];
         Mfma<T>::unit(o[i], vf, pf);
       }
+    }
+    if constexpr (kBf16) {
+      // the same for the value fragments of O^T += V^T P^T
+      constexpr int NM = NU_PV * HD / 32, VLA = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, VLA, 0);
+#pragma unroll
+      for (int i = 0; i < NM - VLA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, VLA, 0);
     }
 
     }
