@@ -111,13 +111,6 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   const int qi = qt * QT + wave * 32 + l32;
   const int qc = min(qi, L - 1);
   const T* qrow = q + ((size_t)task * L + qc) * D + (size_t)h * HD;
-  u32x4 qf[NU_QK];
-#pragma unroll
-  for (int u = 0; u < NU_QK; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + (2 * u + g) * VEC);
-  // take the Q loads' wait here, before the key/value copies are in flight:
-  // a wait inside the tile loop would also wait for those copies
-#pragma unroll
-  for (int u = 0; u < NU_QK; ++u) asm volatile("" : "+v"(qf[u]));
 
   // Key/value tiles are copied from the pool straight into LDS: each copy
   // instruction moves one 1 KB block (64 lanes x 16 bytes); a lane fetches the
@@ -216,6 +209,15 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
 
   const int n_tiles = (n_keys + KT - 1) / KT;
   for (int t = 0; t < NSTG - 1 && t < n_tiles; ++t) copy_tile(t);
+  // The Q fragments load while the first tiles' copies are in flight; their
+  // wait is taken here together with the first tile's (a wait first inside
+  // the tile loop would also wait for the next tile's copies).
+  u32x4 qf[NU_QK];
+#pragma unroll
+  for (int u = 0; u < NU_QK; ++u) qf[u] = *reinterpret_cast<const u32x4*>(qrow + (2 * u + g) * VEC);
+  vm_wait_n((min(NSTG - 2, n_tiles - 1)) * DPW);
+#pragma unroll
+  for (int u = 0; u < NU_QK; ++u) asm volatile("" : "+v"(qf[u]));
   for (int tile = 0; tile < n_tiles; ++tile) {
     // tile lands (copies of later tiles may stay in flight); the barrier also
     // tells every wave that all reads of the stage about to be refilled are done
