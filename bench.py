@@ -58,6 +58,14 @@ def kernel_work(cfg, n_tasks, n_read):
     }
 
 
+def cache_bytes(cfg, n_tasks, n_read):
+    """Cached keys and values an attention launch reads (algorithmic bytes):
+    the window's noisy KV for self-attention, the context K/V for cross."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    return {"attn_self": n_tasks * (n_read + 1) * cfg.tokens * cfg.hidden * 2 * es,
+            "attn_cross": n_tasks * cfg.n_ctx * cfg.hidden * 2 * es}
+
+
 def setup_stage(cfg, n_tasks, seed=0):
     """Device-resident weights, pool, contexts and inputs for single-stage runs."""
     import torch
@@ -732,6 +740,7 @@ def main():
     flops_step = n_tasks * stage_flops(cfg, n_read)
     peak = PEAK[cfg.dtype]
     work = kernel_work(cfg, n_tasks, n_read)
+    kv = cache_bytes(cfg, n_tasks, n_read)
     kernels = {}
     for name, (launches, ms) in trace.items():
         avg_ms = ms / max(launches, 1)
@@ -742,6 +751,8 @@ def main():
                 rec["tflops"] = round(amount / (avg_ms * 1e-3) / 1e12, 1)
             else:
                 rec["gbs"] = round(amount / (avg_ms * 1e-3) / 1e9, 1)
+        if name in kv:
+            rec["kv_gbs"] = round(kv[name] / (avg_ms * 1e-3) / 1e9, 1)
         kernels[name] = rec
     dom = max((n for n in trace if n in work), key=lambda n: trace[n][1])
     kind, amount = work[dom]
