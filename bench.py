@@ -575,20 +575,23 @@ def trace_summary(dirs):
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when there is none or the kernel's source changed since it was taken."""
+    None when there is none or the kernel's source changed since it was taken.
+    profiles/traffic.json: {"workload", "copy_fetch_scale", "copy_write_scale",
+    "kernels": {name: {"fetch_kib", "write_kib", "sources": {path: sha256}}}}."""
     import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    if rec.get("kernel") != kernel:
+    doc = json.load(open(path))
+    rec = doc.get("kernels", {}).get(kernel)
+    if rec is None:
         return None
-    root = os.path.dirname(os.path.abspath(__file__))
     for rel, digest in rec["sources"].items():
         f = os.path.join(root, rel)
         if not os.path.exists(f) or hashlib.sha256(open(f, "rb").read()).hexdigest() != digest:
             return None
-    kib = rec["fetch_kib"] * rec["copy_fetch_scale"] + rec["write_kib"] * rec["copy_write_scale"]
+    kib = rec["fetch_kib"] * doc["copy_fetch_scale"] + rec["write_kib"] * doc["copy_write_scale"]
     return int(round(kib * 1024))
 
 
