@@ -25,9 +25,10 @@
 // waves stalls instruction issue while the memory pipeline drains it, and with
 // one wave per SIMD nothing else keeps the matrix cores busy meanwhile.
 //
-// Tile order: workgroups walk the tile grid in groups of two tile rows; with
-// 32 or more tile columns each XCD takes a contiguous range of that order,
-// else the dispatch order deals the tiles round-robin over the 8 XCDs.
+// Tile order: workgroups walk the tile grid in groups of two tile rows; for
+// QKV and with 32 or more tile columns each XCD takes a contiguous range of
+// that order, else the dispatch order deals the tiles round-robin over the
+// 8 XCDs.
 #include <type_traits>
 
 #include "common.h"
@@ -363,16 +364,16 @@ __global__ void __launch_bounds__(64 * NW) k_gemm(const T* __restrict__ A, const
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   constexpr int GROUP = 2;
-  // Consecutive workgroups go to the 8 XCDs in turn.  With many tile columns
-  // each XCD takes a contiguous range of the grouped order instead, so that
-  // the tiles its CUs run at one time share few A and B panels in its L2 (and
-  // the QKV epilogue's keys and values of a task are written from the XCD
-  // whose L2 the task's attention reads them from); with few tile columns
-  // the dispatch order measured faster.
+  // Consecutive workgroups go to the 8 XCDs in turn.  With many tile columns,
+  // and always for QKV, each XCD takes a contiguous range of the grouped order
+  // instead, so that the tiles its CUs run at one time share few A and B
+  // panels in its L2 and the QKV epilogue writes a task's keys and values
+  // from the XCD whose L2 the task's attention reads them from; with few tile
+  // columns the dispatch order measured faster for the other GEMMs.
   const int total = tiles_m * tiles_n;
   const int full = (total / 8) * 8;
   const int bid = blockIdx.x;
-  const int pid = (tiles_n < 32 || bid >= full) ? bid : (bid % 8) * (total / 8) + bid / 8;
+  const int pid = ((tiles_n < 32 && EPI != EPI_QKV) || bid >= full) ? bid : (bid % 8) * (total / 8) + bid / 8;
   const int per_group = GROUP * tiles_n;
   const int first_m = (pid / per_group) * GROUP;
   const int gsz = min(tiles_m - first_m, GROUP);
