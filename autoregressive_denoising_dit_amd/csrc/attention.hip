@@ -146,11 +146,11 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   const uint32_t my_dst = (uint32_t)__builtin_amdgcn_readfirstlane(
       k_wave ? wave * DPW * 1024 : KT * KCH * 16 + (wave * DPW - KB) * 1024);
   const T* cur_base = seg_base(0);   // base of segment f_seg
-  auto copy_tile = [&](int tile) {
+  auto copy_tile = [&](int tile, int stg) {
     const int t0 = tile * KT;
     const T* b0 = cur_base;
     const int split = seg_len - f_off;   // tile-relative key where the next segment starts
-    const uint32_t stage = lds0 + (uint32_t)((tile % NSTG) * TILE_CH * 16);
+    const uint32_t stage = lds0 + (uint32_t)(stg * TILE_CH * 16);
     if (split >= KT && t0 + KT <= n_keys) {
       // a buffer resource over this head's K (or V^T) of the segment; the tile
       // offset goes in the scalar offset, the lane's in the 32-bit vector one.
@@ -208,7 +208,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   for (int r = 0; r < 16; ++r) negm[r] = 0.0f;
 
   const int n_tiles = (n_keys + KT - 1) / KT;
-  for (int t = 0; t < NSTG - 1 && t < n_tiles; ++t) copy_tile(t);
+  for (int t = 0; t < NSTG - 1 && t < n_tiles; ++t) copy_tile(t, t);
   // The Q fragments load while the first tiles' copies are in flight; their
   // wait is taken here together with the first tile's (a wait first inside
   // the tile loop would also wait for the next tile's copies).
@@ -218,13 +218,22 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
   vm_wait_n((min(NSTG - 2, n_tiles - 1)) * DPW);
 #pragma unroll
   for (int u = 0; u < NU_QK; ++u) asm volatile("" : "+v"(qf[u]));
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  // In bf16 the loop runs NSTG tiles per iteration, one per LDS stage, so
+  // that each stage's LDS offset is a constant folded into the fragment
+  // reads' offset field instead of an address add per read.
+  constexpr int UNR = kBf16 ? NSTG : 1;
+  for (int tile0 = 0; tile0 < n_tiles; tile0 += UNR) {
+#pragma unroll
+  for (int su = 0; su < UNR; ++su) {
+    const int tile = tile0 + su;
+    if (tile >= n_tiles) break;
+    const int st = kBf16 ? su : tile % NSTG;   // LDS stage of this tile
     // tile lands (copies of later tiles may stay in flight); the barrier also
     // tells every wave that all reads of the stage about to be refilled are done
     vm_wait_n((min(tile + NSTG - 2, n_tiles - 1) - tile) * DPW);
     __syncthreads();
-    if (tile + NSTG - 1 < n_tiles) copy_tile(tile + NSTG - 1);
-    const u32x4* ks = smem + (tile % NSTG) * TILE_CH;
+    if (tile + NSTG - 1 < n_tiles) copy_tile(tile + NSTG - 1, (st + NSTG - 1) % NSTG);
+    const u32x4* ks = smem + st * TILE_CH;
     const u32x4* vs = ks + KT * KCH;
 
     if (wave_active) {
@@ -341,6 +350,7 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
     }
 
     }
+  }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
