@@ -276,13 +276,13 @@ k_attn(const T* __restrict__ q, T* __restrict__ out, int ldo, PoolGeo pg, const 
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[t][r]);
+      for (int r = 0; r < 16; ++r) mt = __builtin_elementwise_maximum(mt, s[t][r]);
     {
       // the other half-wave's keys of the same query: swap the lane halves in
       // registers (v_permlane32_swap) instead of a round trip through LDS,
       // which would also wait for the fragment reads in flight
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mt), __float_as_int(mt), false, false);
-      mt = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+      mt = __builtin_elementwise_maximum(__int_as_float(sw[0]), __int_as_float(sw[1]));
     }
     const bool need = (tile == 0) || (mt > kLazy);
     if (__any(need)) {
