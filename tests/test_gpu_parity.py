@@ -336,6 +336,28 @@ def test_stage_two_frame_chunks():
     _check_probe(case)
 
 
+def test_stage_batch_rows_matches_stage_batch_bitwise():
+    """ps_stage_batch_rows, each task's rows in a tensor of its own (task 0
+    updated in place), gives ps_stage_batch's stage outputs and cache entries
+    bit for bit: the rows are gathered into the workspace, run as one batch
+    and scattered back.  Task 2 reads the entry task 0 writes in the batch."""
+    cfg = with_(C2, hidden=512, heads=8, head_dim=64, ffn=1024, n_ctx=200)
+    tasks = [(0, 5, 1, 3), (1, 4, 2, 2), (0, 6, 1, 3)]
+    a = StageCase(cfg, tasks, n_slots=cfg.window + 2).run_gpu()
+    b = StageCase(cfg, tasks, n_slots=cfg.window + 2)
+    ps_tasks = b.setup_gpu()
+    L = cfg.tokens
+    rows_in = [to_dev(b.h_in[i * L:(i + 1) * L], torch.float32) for i in range(len(tasks))]
+    rows_out = [rows_in[0]] + [torch.empty_like(r) for r in rows_in[1:]]
+    say("stage_batch_rows", cfg.name, tasks)
+    runtime.stage_batch_rows(b.pool, b.block, b.te, ps_tasks, rows_in, rows_out)
+    torch.cuda.synchronize()
+    for i, (sg, c, s, _) in enumerate(tasks):
+        assert np.array_equal(host(rows_out[i]), a.gpu_h_out[i * L:(i + 1) * L]), i
+        k, v = b.pool.fetch(sg, 0, s, c % b.R)
+        assert np.array_equal(host(k), a.gpu_kv[(sg, c, s)][0]) and np.array_equal(host(v), a.gpu_kv[(sg, c, s)][1])
+
+
 def test_stage_rope_tables_beyond_lds():
     """A 60 x 88 token grid: the row and column RoPE tables (3152 pairs with the
     frame rows) exceed the QKV epilogue's LDS budget, so the epilogue reads
