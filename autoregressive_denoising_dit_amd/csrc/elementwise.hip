@@ -223,14 +223,30 @@ __global__ void __launch_bounds__(256) k_gemv(const float* __restrict__ x, int K
   if (lane == 0) y[n] = acc + b[n];
 }
 
-// One thread copies the table word by word with a uniform index, so the
-// argument is read straight from the kernel-argument segment.
+// One wave copies the table: lane l takes words l, l + 64, ..., read straight
+// from the kernel-argument segment (vector loads at the argument's address),
+// all loads issued before the first store, so that the copy costs about one
+// round trip to the argument memory instead of one per cache line.
 __global__ void k_put_tasks(TaskTable tt, DevTask* dst) {
-  if (threadIdx.x != 0) return;
-  const int words = tt.n * (int)(sizeof(DevTask) / 4);
+  constexpr int W = PS_MAX_TASKS * (int)(sizeof(DevTask) / 4);   // words of the whole array
+  constexpr int PER = (W + 63) / 64;
   const int32_t* src = reinterpret_cast<const int32_t*>(&tt.t[0]);
   int32_t* out = reinterpret_cast<int32_t*>(dst);
-  for (int i = 0; i < words; ++i) out[i] = src[i];
+  int32_t v[PER];
+  // the loads do not wait for the task count: every word of the array is read
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = k * 64 + (int)threadIdx.x;
+    v[k] = (k * 64 + 64 <= W || i < W) ? src[i] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) asm volatile("" : "+v"(v[k]));   // all loaded here, none sunk below
+  const int words = tt.n * (int)(sizeof(DevTask) / 4);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = k * 64 + (int)threadIdx.x;
+    if (i < words) out[i] = v[k];
+  }
 }
 
 struct Dts {
