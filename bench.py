@@ -643,8 +643,8 @@ def cpu_baseline_interval(cfg):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c5", choices=["c2", "c5", "c3", "c4", "placement", "placed"],
                     help="c5 (default) / c2: one stage batch per step; c3 / c4: the staggered schedule "
                          "over all blocks and steps, reporting the chunk interval; placement: block-batch "
