@@ -197,38 +197,40 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
       lt.y = tb2 + tg.off_y;
       lt.x = tb2 + tg.off_x;
       RopePtrs gt{ep.rope_f + (size_t)tg.t0 * pg.frames * (pg.seg_f / 2), pg.rope_y, pg.rope_x};
-      const bool in_lds = ep.rope_tab != 0;
-      for (int r = rq; r < nrows; r += 4) {
-        const int row = rbase + r;
-        const int ti = (int)pg.div_L.div(row);
-        const int tok = row - ti * pg.L;
-        const int yx = (int)pg.div_cols.div(tok);
-        const int fl = (int)pg.div_plane.div(tok);
-        const int yy = yx - (int)pg.div_rows.div(yx) * pg.rows;
-        const int xx = tok - yx * pg.cols;
-        float2 c0, c1;
-        if (in_lds) {
-          c0 = rope_cs(lt, pg, ti - tg.t0, fl, yy, xx, dd);
-          c1 = rope_cs(lt, pg, ti - tg.t0, fl, yy, xx, dd + 2);
-        } else {
-          c0 = rope_cs(gt, pg, ti - tg.t0, fl, yy, xx, dd);
-          c1 = rope_cs(gt, pg, ti - tg.t0, fl, yy, xx, dd + 2);
+      // One loop per table location, so that the tables' pointers keep their
+      // address space: a pointer that may be either LDS or global memory is
+      // read with a flat load, and the wait for a flat load also waits for
+      // every store issued before it -- each row would wait for the previous
+      // rows' stores to complete.
+      auto rows = [&](const RopePtrs& tb) __attribute__((always_inline)) {
+        for (int r = rq; r < nrows; r += 4) {
+          const int row = rbase + r;
+          const int ti = (int)pg.div_L.div(row);
+          const int tok = row - ti * pg.L;
+          const int yx = (int)pg.div_cols.div(tok);
+          const int fl = (int)pg.div_plane.div(tok);
+          const int yy = yx - (int)pg.div_rows.div(yx) * pg.rows;
+          const int xx = tok - yx * pg.cols;
+          const float2 c0 = rope_cs(tb, pg, ti - tg.t0, fl, yy, xx, dd);
+          const float2 c1 = rope_cs(tb, pg, ti - tg.t0, fl, yy, xx, dd + 2);
+          const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
+          // rotate the pairs (dd, dd + 1) and (dd + 2, dd + 3)
+          f32x4 o;
+          o[0] = v[0] * c0.x - v[1] * c0.y;
+          o[1] = v[1] * c0.x + v[0] * c0.y;
+          o[2] = v[2] * c1.x - v[3] * c1.y;
+          o[3] = v[3] * c1.x + v[2] * c1.y;
+          if (!col_ok) continue;
+          if (part == 0) {
+            store4(static_cast<T*>(ep.out) + (size_t)row * ep.ldo + cc, o * ep.out_scale);
+          } else {
+            T* kb = static_cast<T*>(pg.kv) + soff[ti];
+            store4(kb + ((size_t)hh * pg.L + tok) * pg.d + dd, o);
+          }
         }
-        const f32x4 v = ld4(stg + r * EP + 4 * cq) + bias;
-        // rotate the pairs (dd, dd + 1) and (dd + 2, dd + 3)
-        f32x4 o;
-        o[0] = v[0] * c0.x - v[1] * c0.y;
-        o[1] = v[1] * c0.x + v[0] * c0.y;
-        o[2] = v[2] * c1.x - v[3] * c1.y;
-        o[3] = v[3] * c1.x + v[2] * c1.y;
-        if (!col_ok) continue;
-        if (part == 0) {
-          store4(static_cast<T*>(ep.out) + (size_t)row * ep.ldo + cc, o * ep.out_scale);
-        } else {
-          T* kb = static_cast<T*>(pg.kv) + soff[ti];
-          store4(kb + ((size_t)hh * pg.L + tok) * pg.d + dd, o);
-        }
-      }
+      };
+      if (ep.rope_tab != 0) rows(lt);
+      else rows(gt);
       return;
     }
   } else {
