@@ -261,10 +261,14 @@ __device__ __forceinline__ void epilogue_block(const float* stg, int rbase, int 
 template <int EB>
 __device__ __forceinline__ void load_res(f32x4 (&h)[EB], const float* h_in, int rbase, int nrows, int r0, int rq,
                                          int col, int N) {
+  // lanes past the last column load a valid one (and store nothing): the
+  // loads stay unconditional, so the compiler counts them in order instead
+  // of waiting for each one where branches join
+  const int cc = min(col, N - 4);
 #pragma unroll
   for (int k = 0; k < EB; ++k) {
     const int r = min(r0 + 4 * k + rq, nrows - 1);
-    h[k] = col < N ? ld4(h_in + (size_t)(rbase + r) * N + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    h[k] = ld4(h_in + (size_t)(rbase + r) * N + cc);
   }
 }
 
