@@ -127,7 +127,7 @@ struct DevTask {
 };
 
 // Host-side image of the batch's task list; it travels to device memory as
-// the argument of a one-thread copy kernel (stream-ordered, no host staging).
+// the argument of a one-wave copy kernel (stream-ordered, no host staging).
 struct TaskTable {
   DevTask t[PS_MAX_TASKS];
   int32_t n;
